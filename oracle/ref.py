@@ -1,0 +1,249 @@
+"""CPU oracle for the W4A16 group-quantized linear with a sparse outlier term.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the package smoke check and the CPU
+baseline leg of the benchmark use it.  It shares no code with the HIP
+library (it imports only numpy and the seeded input generator).
+
+What is computed, and where the pages say so
+--------------------------------------------
+* Dense-and-sparse decomposition: the weight matrix is the sum of a dense
+  part that is quantized to a few bits and a sparse part that keeps a small
+  fraction of the weights in fp16; the product is split the same way,
+  W x = W_dense x + W_sparse x (SqueezeLLM explainer, sections 2.2 and 2.3).
+  The sparsity is the count of sparse non-zeros over all weights (section
+  2.2).  The pages select the sparse entries with a Hessian-based
+  sensitivity; with no model or data, the entries of largest |w| are taken
+  instead (ties: lower flat index first).
+* Round-to-nearest (RTN) weight-only quantization is the calibration-free
+  baseline of weight quantization (AWQ paper, section 2; LLM Compressor
+  article, FAQ).  The pages never print its formula.  The reading used
+  here: asymmetric INT4 per group of 128 consecutive input channels
+  ("W4A16 g128", DeepCompressor README perplexity table), step
+  Delta = (max - min) / (2^4 - 1), an integer zero-point, round half to
+  even, clamp to [0, 15].
+* 4-bit packing: eight codes per 32-bit word so that byte-addressed hardware
+  still sees the 4x size cut (AWQ paper, section 1).
+* On-the-fly dequantization inside the linear (AWQ paper, section 1):
+  w_hat = (q - z) * s, and y = x . w_hat^T + W_sparse x.
+
+Precision
+---------
+The quantizer (split, range, scale, zero, codes) is evaluated in IEEE
+float32 with correctly rounded division and no fused multiply-add, because
+its results are integers (codes, zero-points) and fp16 bit patterns that
+must be unique; the same float32 definition is what the device kernels
+implement.  Dequantization and the linear layer run in float64.
+
+Every function states the readings it takes where the pages are silent.
+No function here is "parity unpinned": each is pinned by the CPU tests
+(on-grid exact recovery, zero exactness, brute force in exact rationals,
+closed forms, full sorts on tiny inputs, hand-worked fixtures).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128
+QMAX = 15  # 2^4 - 1 for INT4 codes
+FP16_MIN_NORMAL = np.float32(2.0 ** -14)
+
+
+# --------------------------------------------------------------------------
+# O1: dense-and-sparse split (SqueezeLLM explainer, sections 2.2-2.3)
+# --------------------------------------------------------------------------
+def split_outliers(W: np.ndarray, sparse_k: int):
+    """Split ``W`` into a dense part and an fp16 CSR sparse part.
+
+    The ``sparse_k`` entries of largest |w| go to the sparse part; entries
+    with equal |w| are taken in ascending flat index ``n*K + k``.  The dense
+    part is ``W`` with those entries replaced by +0.0, so that
+    ``W = W_dense + W_sparse`` holds exactly before the fp16 rounding of the
+    sparse values.
+
+    Returns ``(W_dense float32 [N,K], row_ptr int32 [N+1], col int32 [nnz],
+    val float16 [nnz])`` with CSR rows = output channels n and columns
+    strictly ascending inside a row.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    total = N * K
+    if not 0 <= sparse_k <= total:
+        raise ValueError("sparse_k out of range")
+    Wd = W.copy()
+    if sparse_k == 0:
+        return Wd, np.zeros(N + 1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.float16)
+    a = np.abs(W).reshape(-1)
+    # threshold T = the sparse_k-th largest |w|
+    T = np.partition(a, total - sparse_k)[total - sparse_k]
+    above = np.flatnonzero(a > T)
+    ties = np.flatnonzero(a == T)           # ascending flat index
+    need = sparse_k - above.size
+    chosen = np.sort(np.concatenate([above, ties[:need]]))
+    rows = chosen // K
+    cols = chosen % K
+    val = W.reshape(-1)[chosen].astype(np.float16)
+    Wd.reshape(-1)[chosen] = np.float32(0.0)
+    row_ptr = np.zeros(N + 1, np.int64)
+    np.add.at(row_ptr, rows + 1, 1)
+    row_ptr = np.cumsum(row_ptr).astype(np.int32)
+    return Wd, row_ptr, cols.astype(np.int32), val
+
+
+# --------------------------------------------------------------------------
+# O2-O5: RTN group quantizer
+# --------------------------------------------------------------------------
+def quantize_rtn(Wd: np.ndarray, group: int = GROUP):
+    """Asymmetric INT4 round-to-nearest quantization, one (s, z) per group.
+
+    For each row n and group j of ``group`` consecutive input channels:
+
+    * ``mn, mx`` = min and max of the group (zeros left by the split count);
+    * ``d = fl32(fl32(mx - mn) / 15)``, floored at 2^-14 (the smallest
+      normal fp16) so that a constant group still has a usable step;
+    * ``s`` = d rounded to fp16 (nearest even); the codes are computed with
+      this stored value, so the stored metadata reproduces them;
+    * ``z = clamp(rint(fl32(-mn / s)), 0, 15)``, an integer stored as fp16;
+    * ``q = clamp(rint(fl32(w / s)) + z, 0, 15)``.
+
+    ``rint`` is round-half-to-even.  Returns ``(q uint8 [N,K], s float16
+    [N,K/group], z float16 [N,K/group])``.
+    """
+    Wd = np.asarray(Wd, dtype=np.float32)
+    N, K = Wd.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    G = K // group
+    Wg = Wd.reshape(N, G, group)
+    mn = Wg.min(axis=2)
+    mx = Wg.max(axis=2)
+    rng = (mx - mn).astype(np.float32)
+    d = (rng / np.float32(QMAX)).astype(np.float32)
+    d = np.maximum(d, FP16_MIN_NORMAL)
+    s16 = d.astype(np.float16)
+    s = s16.astype(np.float32)
+    zf = np.rint((-mn) / s).astype(np.float32)
+    z = np.clip(zf, 0, QMAX).astype(np.int32)
+    t = np.rint(Wg / s[:, :, None]).astype(np.float32)
+    q = np.clip(t + z[:, :, None].astype(np.float32), 0, QMAX).astype(np.uint8)
+    return q.reshape(N, K), s16, z.astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# O6: packing (AWQ paper, section 1: 4-bit weight packing)
+# --------------------------------------------------------------------------
+def pack(q: np.ndarray) -> np.ndarray:
+    """Eight consecutive codes along K per uint32; code k = 8t + i sits in
+    bits [4i, 4i + 4) of word t."""
+    q = np.asarray(q, dtype=np.uint8)
+    N, K = q.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    q8 = q.reshape(N, K // 8, 8).astype(np.uint32)
+    out = np.zeros((N, K // 8), np.uint32)
+    for i in range(8):
+        out |= q8[:, :, i] << np.uint32(4 * i)
+    return out
+
+
+def unpack(packed: np.ndarray) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint32)
+    N, W = packed.shape
+    q = np.empty((N, W, 8), np.uint8)
+    for i in range(8):
+        q[:, :, i] = (packed >> np.uint32(4 * i)) & np.uint32(0xF)
+    return q.reshape(N, W * 8)
+
+
+# --------------------------------------------------------------------------
+# O7-O8: dequantization and the linear layer, float64
+# --------------------------------------------------------------------------
+def dequant(q: np.ndarray, s: np.ndarray, z: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """w_hat[n, k] = (q[n, k] - z[n, k // group]) * s[n, k // group] in float64."""
+    q = np.asarray(q)
+    N, K = q.shape
+    G = K // group
+    qg = q.reshape(N, G, group).astype(np.float64)
+    zf = np.asarray(z).astype(np.float64)[:, :, None]
+    sf = np.asarray(s).astype(np.float64)[:, :, None]
+    return ((qg - zf) * sf).reshape(N, K)
+
+
+def sparse_term(x: np.ndarray, row_ptr, col, val, N: int) -> np.ndarray:
+    """(W_sparse x)^T for all rows of x: out[m, n] = sum_e val_e * x[m, col_e]
+    over the CSR entries e of row n, in float64."""
+    x64 = np.asarray(x).astype(np.float64)
+    M = x64.shape[0]
+    out = np.zeros((M, N), np.float64)
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    nnz = int(row_ptr[-1]) if row_ptr.size else 0
+    if nnz == 0:
+        return out
+    col = np.asarray(col, dtype=np.int64)[:nnz]
+    v = np.asarray(val).astype(np.float64)[:nnz]
+    prod = x64[:, col] * v[None, :]           # [M, nnz]
+    counts = np.diff(row_ptr)
+    nonempty = np.flatnonzero(counts)
+    sums = np.add.reduceat(prod, row_ptr[nonempty], axis=1)
+    out[:, nonempty] = sums
+    return out
+
+
+def linear_ref(x, q, s, z, row_ptr=None, col=None, val=None, group: int = GROUP):
+    """y[m, n] = sum_k x[m, k] * w_hat[n, k] + (W_sparse x)[n, m] in float64.
+
+    ``q`` may be the unpacked codes [N, K] (uint8) or the packed words
+    [N, K/8] (uint32)."""
+    q = np.asarray(q)
+    if q.dtype == np.uint32:
+        q = unpack(q)
+    N = q.shape[0]
+    W_hat = dequant(q, s, z, group)
+    y = np.asarray(x).astype(np.float64) @ W_hat.T
+    if row_ptr is not None:
+        y += sparse_term(x, row_ptr, col, val, N)
+    return y
+
+
+def linear_rows(x, q, s, z, rows, row_ptr=None, col=None, val=None, group: int = GROUP):
+    """The same as ``linear_ref`` restricted to output channels ``rows``
+    (used to check full-size outputs one sample at a time)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    q = np.asarray(q)
+    if q.dtype == np.uint32:
+        qs = unpack(q[rows])
+    else:
+        qs = q[rows]
+    W_hat = dequant(qs, np.asarray(s)[rows], np.asarray(z)[rows], group)
+    x64 = np.asarray(x).astype(np.float64)
+    y = x64 @ W_hat.T
+    if row_ptr is not None:
+        row_ptr = np.asarray(row_ptr, dtype=np.int64)
+        col = np.asarray(col, dtype=np.int64)
+        v = np.asarray(val).astype(np.float64)
+        for j, n in enumerate(rows):
+            a, b = row_ptr[n], row_ptr[n + 1]
+            if b > a:
+                y[:, j] += x64[:, col[a:b]] @ v[a:b]
+    return y
+
+
+def quantize_layer(W: np.ndarray, sparse_k: int = 0, group: int = GROUP):
+    """The offline pipeline: split, quantize the dense part, pack."""
+    Wd, row_ptr, col, val = split_outliers(W, sparse_k)
+    q, s, z = quantize_rtn(Wd, group)
+    return dict(W_dense=Wd, q=q, s=s, z=z, packed=pack(q), row_ptr=row_ptr, col=col, val=val)
+
+
+def rel_err_inf(y, y_ref) -> float:
+    """max |y - y_ref| / max |y_ref|, the parity measure for floating outputs."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    den = np.max(np.abs(y_ref)) if y_ref.size else 0.0
+    num = np.max(np.abs(y - y_ref)) if y_ref.size else 0.0
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
+
+
+TOL = 5e-3  # ||y - y_ref||_inf <= TOL * ||y_ref||_inf

@@ -1,0 +1,341 @@
+"""Pins for the CPU oracle, checked against what the pages and mathematics fix.
+
+None of these tests re-types the oracle's formulas: each checks a property
+that a plausible mistake (dropped zero-point, wrong sign, wrong group index,
+transposed operand, wrong nibble order, wrong tie-break) would break.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f16_bits(a):
+    return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_hand_words():
+    # codes 0..7 along K land in nibbles 0..7: the word reads 0x76543210
+    q = np.arange(8, dtype=np.uint8)[None, :]
+    assert oracle.pack(q)[0, 0] == 0x76543210
+    q = np.array([[15, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1]], np.uint8)
+    w = oracle.pack(q)
+    assert w[0, 0] == 0x0000000F and w[0, 1] == 0x10000000
+    q = np.full((2, 8), 0xA, np.uint8)
+    q[1] = [1, 2, 3, 4, 5, 6, 7, 8]
+    assert list(oracle.pack(q)[:, 0]) == [0xAAAAAAAA, 0x87654321]
+
+
+def test_pack_roundtrip():
+    rng = np.random.default_rng(1)
+    q = rng.integers(0, 16, size=(7, 256), dtype=np.uint8)
+    p = oracle.pack(q)
+    assert p.shape == (7, 32) and p.dtype == np.uint32
+    assert np.array_equal(oracle.unpack(p), q)
+    # nibble i of word t is code 8t+i, checked with plain integer division
+    for n, t, i in [(0, 0, 0), (3, 5, 7), (6, 31, 3)]:
+        assert (int(p[n, t]) // 16 ** i) % 16 == q[n, 8 * t + i]
+
+
+# ---------------------------------------------------------------- quantizer
+def _on_grid(seed, N, G, group=128):
+    """Weights already on a quantization grid: w = (q - z) * s with s a normal
+    fp16, z in [0, 15] and every group holding codes 0 and 15."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(-14, -1, size=(N, G))
+    m = rng.integers(0, 1024, size=(N, G))
+    s16 = ((1.0 + m / 1024.0) * 2.0 ** e).astype(np.float16)
+    z = rng.integers(0, 16, size=(N, G))
+    q = rng.integers(0, 16, size=(N, G, group))
+    for n in range(N):
+        for g in range(G):
+            a, b = rng.choice(group, 2, replace=False)
+            q[n, g, a] = 0
+            q[n, g, b] = 15
+    s32 = s16.astype(np.float32)
+    w = ((q - z[:, :, None]).astype(np.float32) * s32[:, :, None]).astype(np.float32)
+    return w.reshape(N, G * group), q.reshape(N, G * group).astype(np.uint8), s16, z
+
+
+@pytest.mark.parametrize("seed,N,G", [(0, 3, 1), (1, 8, 4), (2, 5, 7)])
+def test_on_grid_exact_recovery(seed, N, G):
+    w, q, s16, z = _on_grid(seed, N, G)
+    # the construction is exact in float32
+    assert np.array_equal(((q.reshape(N, G, 128) - z[:, :, None]) * s16.astype(np.float64)[:, :, None]).reshape(N, -1),
+                          w.astype(np.float64))
+    q2, s2, z2 = oracle.quantize_rtn(w)
+    assert np.array_equal(f16_bits(s2), f16_bits(s16))
+    assert np.array_equal(z2.astype(np.int64), z)
+    assert np.array_equal(q2, q)
+
+
+def test_golden_hand_cases():
+    with open(os.path.join(GOLDEN, "rtn_hand_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        g = np.full(128, c["fill"], np.float32)
+        for k, v in c["entries"].items():
+            g[int(k)] = v
+        q, s, z = oracle.quantize_rtn(g[None, :])
+        assert f16_bits(s)[0, 0] == int(c["scale_bits"], 16), c["name"]
+        assert f16_bits(z)[0, 0] == int(c["zero_bits"], 16), c["name"]
+        for k in range(128):
+            want = c["codes"].get(str(k), c["fill_code"])
+            assert q[0, k] == want, (c["name"], k)
+
+
+def _cfg1_small():
+    W, x, cfg = workloads.make(1)
+    return W, x
+
+
+def test_zero_dequantizes_to_exact_zero():
+    W, _ = _cfg1_small()
+    W = W.copy()
+    rng = np.random.default_rng(5)
+    W.reshape(-1)[rng.choice(W.size, 4000, replace=False)] = 0.0
+    q, s, z = oracle.quantize_rtn(W)
+    w_hat = oracle.dequant(q, s, z)
+    assert np.all(w_hat[W == 0.0] == 0.0)
+
+
+def test_group_minimum_gets_code_zero():
+    W, _ = _cfg1_small()
+    q, s, z = oracle.quantize_rtn(W)
+    N, K = W.shape
+    G = K // 128
+    Wg = W.reshape(N, G, 128)
+    qg = q.reshape(N, G, 128)
+    amin = Wg.argmin(axis=2)
+    for n in range(N):
+        for g in range(G):
+            zz = int(z[n, g])
+            if 0 < zz < 15:
+                assert qg[n, g, amin[n, g]] == 0
+
+
+def test_brute_force_exact_rationals():
+    """Each code is the nearest grid point in exact arithmetic; the scale is the
+    fp16 nearest to range/15 and the zero-point the nearest integer to -min/s."""
+    W = workloads.random_weights(11, 4, 256, sigma=0.02)
+    W[1, 5] *= 20
+    W[2, 200] *= -20
+    W[3, 0:128] = np.abs(W[3, 0:128])          # an all-positive group (clamped z)
+    q, s, z = oracle.quantize_rtn(W)
+    near_half = []
+    for n in range(W.shape[0]):
+        for g in range(2):
+            grp = [Fraction(float(v)) for v in W[n, 128 * g:128 * g + 128]]
+            mn, mx = min(grp), max(grp)
+            S = Fraction(float(s[n, g]))
+            Z = int(z[n, g])
+            # scale: within half an fp16 ulp of the exact range/15 (plus the
+            # float32 rounding of the range and quotient)
+            exact = (mx - mn) / 15
+            ulp = Fraction(2) ** (int(np.floor(np.log2(float(S)))) - 10)
+            assert abs(S - exact) <= ulp / 2 + exact * Fraction(1, 2 ** 22)
+            # zero-point: nearest integer to -mn/S, clamped to [0, 15]
+            zc = min(15, max(0, round(-mn / S)))
+            assert Z == zc
+            for k, w in enumerate(grp):
+                errs = [abs(w - (c - Z) * S) for c in range(16)]
+                best = min(errs)
+                winners = {c for c in range(16) if errs[c] == best}
+                qq = int(q[n, 128 * g + k])
+                if qq not in winners:
+                    frac = (w / S) - int(w / S)
+                    near_half.append((n, g, k, float(frac)))
+    assert near_half == []
+
+
+def test_rounding_error_bound_full_config1():
+    W, _ = _cfg1_small()
+    q, s, z = oracle.quantize_rtn(W)
+    w_hat = oracle.dequant(q, s, z)
+    S = np.repeat(s.astype(np.float64), 128, axis=1)
+    inner = (q > 0) & (q < 15)
+    err = np.abs(w_hat - W.astype(np.float64))
+    # RTN: interior codes are within half a step (plus float32 quotient rounding)
+    assert np.all(err[inner] <= S[inner] * (0.5 + 2.0 ** -20))
+    # outlier-free groups keep every weight within half a step of the grid
+    assert np.max(err / S) <= 0.5 + 2.0 ** -20 or np.any(~inner)
+
+
+# ---------------------------------------------------------------- split
+def _tie_heavy(seed, N, K):
+    rng = np.random.default_rng(seed)
+    W = (rng.integers(-8, 9, size=(N, K)) * 0.25).astype(np.float32)
+    return W
+
+
+@pytest.mark.parametrize("seed,N,K,k", [(0, 4, 16, 5), (1, 6, 24, 17), (2, 3, 40, 1),
+                                        (3, 5, 32, 0), (4, 2, 16, 32)])
+def test_split_matches_full_stable_sort(seed, N, K, k):
+    W = _tie_heavy(seed, N, K)
+    Wd, row_ptr, col, val = oracle.split_outliers(W, k)
+    flat = W.reshape(-1)
+    order = sorted(range(flat.size), key=lambda i: (-abs(float(flat[i])), i))
+    chosen = sorted(order[:k])
+    got = [int(r) * K + int(c) for r in range(N) for c in col[row_ptr[r]:row_ptr[r + 1]]]
+    assert got == chosen
+    assert row_ptr[0] == 0 and row_ptr[-1] == k and np.all(np.diff(row_ptr) >= 0)
+    for r in range(N):
+        seg = col[row_ptr[r]:row_ptr[r + 1]]
+        assert np.all(np.diff(seg) > 0)
+    assert np.array_equal(val.astype(np.float32), flat[chosen].astype(np.float16).astype(np.float32))
+    dense = Wd.reshape(-1)
+    assert np.all(dense[chosen] == 0) and not np.any(np.signbit(dense[chosen]))
+    rest = np.setdiff1d(np.arange(flat.size), chosen)
+    assert np.array_equal(dense[rest], flat[rest])
+
+
+def test_split_partition_invariants_config3_shape():
+    W = workloads.random_weights(3000, 256, 512)
+    k = workloads.sparse_k_for(workloads.CONFIGS[3], 256, 512)
+    Wd, row_ptr, col, val = oracle.split_outliers(W, k)
+    sel = np.zeros(W.shape, bool)
+    rows = np.repeat(np.arange(256), np.diff(row_ptr))
+    sel[rows, col] = True
+    assert sel.sum() == k == 589
+    assert np.abs(W[sel]).min() >= np.abs(W[~sel]).max()
+    recomposed = Wd.astype(np.float64)
+    recomposed[rows, col] += val.astype(np.float64)
+    diff = np.abs(recomposed - W)
+    assert np.all(diff[~sel] == 0)
+    assert np.all(diff[sel] <= np.abs(W[sel]) * 2.0 ** -11)
+
+
+def test_config_sizes():
+    c = workloads.CONFIGS
+    assert c[1].n_planted == 1310 and c[2].n_planted == 45088
+    assert c[3].sparse_k == 75497 and c[5].sparse_k == 117440
+    assert c[1].sparse_k == c[2].sparse_k == c[4].sparse_k == 0
+
+
+def test_generator_is_seeded():
+    W1, x1, _ = workloads.make(1)
+    W2, x2, _ = workloads.make(1)
+    assert np.array_equal(W1, W2) and np.array_equal(x1.view(np.uint16), x2.view(np.uint16))
+    assert W1.dtype == np.float32 and x1.dtype == np.float16
+    assert (np.abs(W1) > 0.1).sum() > 900           # the planted x20 outliers (5 sigma otherwise)
+    W4, x4, _ = workloads.make(4, M=4, N=8, K=256)
+    big = np.flatnonzero(np.abs(x4.astype(np.float32)).max(axis=0) > 10)
+    assert 1 <= big.size <= 8
+
+
+# ---------------------------------------------------------------- linear
+def _exact_linear(x, q, s, z, row_ptr, col, val):
+    M, K = x.shape
+    N = q.shape[0]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                g = k // 128
+                acc += Fraction(float(x[m, k])) * (int(q[n, k]) - int(z[n, g])) * Fraction(float(s[n, g]))
+            for e in range(row_ptr[n], row_ptr[n + 1]):
+                acc += Fraction(float(val[e])) * Fraction(float(x[m, col[e]]))
+            out[m][n] = acc
+    return out
+
+
+def test_linear_brute_force_rationals():
+    M, N, K = 3, 5, 256
+    W = workloads.random_weights(21, N, K)
+    x = workloads.random_x(22, M, K)
+    L = oracle.quantize_layer(W, sparse_k=9)
+    y = oracle.linear_ref(x, L["packed"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    assert y.shape == (M, N)
+    ex = _exact_linear(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    for m in range(M):
+        for n in range(N):
+            assert abs(y[m, n] - float(ex[m][n])) <= 1e-12 * max(1.0, abs(float(ex[m][n])))
+
+
+def test_one_hot_x_reads_a_column_of_w_hat():
+    N, K = 6, 384
+    W = workloads.random_weights(31, N, K)
+    q, s, z = oracle.quantize_rtn(W)
+    for k in (0, 127, 128, 300):
+        x = np.zeros((1, K), np.float16)
+        x[0, k] = 1.0
+        y = oracle.linear_ref(x, q, s, z)
+        g = k // 128
+        want = [(int(q[n, k]) - int(z[n, g])) * float(s[n, g]) for n in range(N)]
+        assert np.array_equal(y[0], np.array(want))
+
+
+def test_integer_case_is_exact():
+    x, q, s, z, rp, col, val = workloads.integer_case(7, 4, 6, 512, nnz_per_row=3)
+    y = oracle.linear_ref(x, oracle.pack(q), s, z, rp, col, val)
+    # the same sum in integers: scales are 2^-e, so 16 * y is an integer
+    xi = x.astype(np.int64)
+    s16 = (s.astype(np.float64) * 16).astype(np.int64)
+    W16 = (q.astype(np.int64).reshape(6, 4, 128) - z.astype(np.int64)[:, :, None]) * s16[:, :, None]
+    y16 = xi @ W16.reshape(6, 512).T
+    for n in range(6):
+        for e in range(rp[n], rp[n + 1]):
+            y16[:, n] += 16 * int(val[e]) * xi[:, col[e]]
+    assert np.array_equal(y * 16, y16.astype(np.float64))
+
+
+def test_decomposition_and_sparse_two_ways():
+    M, N, K = 4, 32, 512
+    W = workloads.random_weights(41, N, K)
+    x = workloads.random_x(42, M, K)
+    L = oracle.quantize_layer(W, sparse_k=60)
+    y_full = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    y_dense = oracle.linear_ref(x, L["q"], L["s"], L["z"])
+    # CSR product as a dense matrix built entry by entry
+    Wsp = np.zeros((N, K))
+    for n in range(N):
+        for e in range(L["row_ptr"][n], L["row_ptr"][n + 1]):
+            Wsp[n, L["col"][e]] += float(L["val"][e])
+    y_sp = x.astype(np.float64) @ Wsp.T
+    assert np.allclose(y_full, y_dense + y_sp, rtol=0, atol=1e-12)
+    # the decomposition approximates x W^T for the original weights
+    y_true = x.astype(np.float64) @ W.astype(np.float64).T
+    assert oracle.rel_err_inf(y_full, y_true) < 0.1
+
+
+def test_nnz_zero_reduces_to_dense():
+    W = workloads.random_weights(51, 8, 256)
+    x = workloads.random_x(52, 2, 256)
+    L = oracle.quantize_layer(W, 0)
+    assert L["row_ptr"].tolist() == [0] * 9 and L["col"].size == 0
+    y0 = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    y1 = oracle.linear_ref(x, L["q"], L["s"], L["z"])
+    assert np.array_equal(y0, y1)
+
+
+def test_linear_rows_matches_full():
+    M, N, K = 3, 40, 256
+    W = workloads.random_weights(61, N, K)
+    x = workloads.random_x(62, M, K)
+    L = oracle.quantize_layer(W, 25)
+    y = oracle.linear_ref(x, L["packed"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    rows = [0, 7, 39, 13]
+    ys = oracle.linear_rows(x, L["packed"], L["s"], L["z"], rows, L["row_ptr"], L["col"], L["val"])
+    assert np.allclose(ys, y[:, rows], rtol=1e-13, atol=1e-13)
+
+
+def test_quantization_error_within_tolerance_budget():
+    """The fp16 rounding of (q - z) * s that a kernel may take is far below the
+    5e-3 parity tolerance: checked on config 1 against the oracle itself."""
+    W, x, _ = workloads.make(1)
+    L = oracle.quantize_layer(W, 0)
+    y = oracle.linear_ref(x, L["q"], L["s"], L["z"])
+    w16 = oracle.dequant(L["q"], L["s"], L["z"]).astype(np.float16).astype(np.float64)
+    y16 = x.astype(np.float64) @ w16.T
+    assert oracle.rel_err_inf(y16, y) < 5e-4
