@@ -1,0 +1,250 @@
+"""Benchmark of the W4A16 group-quantized linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--quick]
+
+A step is one call of the online hot path, wq_linear_sparse (kernel chosen by
+M, sparse term fused), on the headline workload: the decode GEMV of a Llama-7B
+MLP up-projection, x fp16 [1, 4096], W [11008, 4096] INT4 g128 (the second
+workload of the task's configuration list).  The weights are quantized and
+packed on the GPU by wq_quantize_rtn / wq_pack before timing (offline steps,
+reported separately under "offline").
+
+Inputs stay resident in HBM: R copies of the layer (packed codes, scales,
+zeros, CSR, x, y) totalling >= 1 GiB are rotated so no launch is served from
+the 256 MB Infinity Cache.  The K timed launches are captured in one HIP graph
+and replayed once between synchronizations; HIP events on the launch stream
+bracket the replay.
+
+Printed: ONE JSON line with the metric (GB/s, algorithmic bytes), the roofline
+of the dominant kernel, the CPU oracle baseline, and the other workloads
+(batched decode + sparse, prefill, the 70B down-projection M sweep).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk, dense
+ROTATE_BYTES = 1 << 30
+
+
+def alg_bytes(M, N, K, nnz, y_bytes=2):
+    """Bytes the method must move: packed codes, fp16 scale+zero, CSR, x, y."""
+    csr = (6 * nnz + 4 * (N + 1)) if nnz else 0
+    return N * K // 2 + N * (K // 128) * 4 + csr + M * K * 2 + M * N * y_bytes
+
+
+def alg_flops(M, N, K, nnz):
+    return 2 * M * N * K + 2 * M * nnz
+
+
+class Layer:
+    """A quantized layer on the GPU, produced by the library's own quantizer."""
+
+    def __init__(self, wq, torch, index, M):
+        W, x, cfg = workloads.make(index, M=M)
+        N, K = W.shape
+        self.N, self.K, self.M = N, K, M
+        self.sparse_k = workloads.sparse_k_for(cfg, N, K)
+        Wd = torch.from_numpy(W).cuda()
+        q = wq.quantize_rtn(Wd, sparse_k=self.sparse_k)
+        self.packed = wq.pack(q["codes"])
+        self.scales, self.zeros = q["scales"], q["zeros"]
+        self.row_ptr, self.col, self.val = q["row_ptr"], q["col"], q["val"]
+        del q, Wd
+        self.x = torch.from_numpy(x.view(np.int16).copy()).cuda().view(torch.float16)
+        torch.cuda.synchronize()
+
+    def sets(self, torch, rotate_bytes):
+        """R independent copies of every input/output, R * bytes >= rotate_bytes."""
+        nb = alg_bytes(self.M, self.N, self.K, self.sparse_k)
+        R = max(1, min(64, math.ceil(rotate_bytes / nb)))
+        out = []
+        for r in range(R):
+            s = dict(x=self.x.clone(), packed=self.packed.clone(), scales=self.scales.clone(),
+                     zeros=self.zeros.clone(), row_ptr=self.row_ptr.clone(), col=self.col.clone(),
+                     val=self.val.clone(),
+                     y=torch.empty((self.M, self.N), dtype=torch.float16, device="cuda"))
+            out.append(s)
+        return out
+
+
+def launch(wq, s, kernel="auto"):
+    wq.linear_sparse(s["x"], s["packed"], s["scales"], s["zeros"], s["row_ptr"], s["col"], s["val"],
+                     out=s["y"], kernel=kernel)
+
+
+def time_launches(wq, torch, sets, steps, warmup, kernel="auto"):
+    """Warm up eagerly, capture `steps` rotating launches in one graph, replay it
+    once between synchronizations; returns milliseconds per launch."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(wq, sets[i % len(sets)], kernel)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            launch(wq, sets[i % len(sets)], kernel)
+    torch.cuda.synchronize()
+    g.replay()  # untimed replay: first replay uploads the graph
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    del g
+    return ms / steps
+
+
+def measure(wq, torch, index, M, steps, warmup, kernel="auto"):
+    L = Layer(wq, torch, index, M)
+    sets = L.sets(torch, ROTATE_BYTES)
+    ms = time_launches(wq, torch, sets, steps, warmup, kernel)
+    nb = alg_bytes(M, L.N, L.K, L.sparse_k)
+    nf = alg_flops(M, L.N, L.K, L.sparse_k)
+    used = kernel if kernel != "auto" else wq.auto_kernel(M, L.N, L.K)
+    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, kernel=used, us_per_launch=ms * 1e3,
+               alg_bytes=nb, alg_flops=nf, GBps=nb / (ms * 1e-3) / 1e9, TFLOPs=nf / (ms * 1e-3) / 1e12,
+               rotated_sets=len(sets))
+    res["hbm_frac"] = res["GBps"] / HBM_PEAK_GBS
+    res["mfma_frac"] = res["TFLOPs"] / MFMA_F16_PEAK_TFS
+    del sets, L
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_offline(wq, torch, index):
+    """Split + quantize + pack of one configuration's weights (offline, once per model)."""
+    W, _, cfg = workloads.make(index, M=1)
+    N, K = W.shape
+    sk = workloads.sparse_k_for(cfg, N, K)
+    Wd = torch.from_numpy(W).cuda()
+    ws = torch.empty(max(1, wq.quantize_workspace_bytes(N, K, sk)), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        q = wq.quantize_rtn(Wd, sparse_k=sk, workspace=ws)
+        wq.pack(q["codes"])
+    torch.cuda.synchronize()
+    reps = 5
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        q = wq.quantize_rtn(Wd, sparse_k=sk, workspace=ws)
+        wq.pack(q["codes"])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    return dict(config=index, N=N, K=K, sparse_k=sk, ms=ms, weights_per_s=N * K / (ms * 1e-3))
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle's linear (fp64 dequantize + BLAS matmul) on the headline
+    workload, on this host's cores, repeated until the time budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    W, x, cfg = workloads.make(2)
+    L = oracle.quantize_layer(W, 0)
+    N, K = W.shape
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while not times or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        oracle.linear_ref(x, L["q"], L["s"], L["z"])
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    nb = alg_bytes(1, N, K, 0)
+    return {"value": nb / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle linear_ref (fp64 dequantize + BLAS) on the full decode layer x[1,4096] "
+                      f"W[11008,4096], median of {len(times)} runs ({t * 1e3:.1f} ms each)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this layer needs no collective and the build targets a single "
+              "MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_gemm_rtn_amd as wq
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wq.load()
+
+    head = measure(wq, torch, 2, 1, args.steps, args.warmup)
+    print(f"# headline: {head}", file=sys.stderr, flush=True)
+    rows = []
+    offline = []
+    if not args.quick:
+        plan = [(3, 16), (4, 2048), (5, 1), (5, 8), (5, 64), (5, 512)]
+        for index, M in plan:
+            steps = max(20, min(args.steps, 100)) if M >= 512 else args.steps
+            r = measure(wq, torch, index, M, steps, min(args.warmup, 10))
+            rows.append(r)
+            print(f"# {r}", file=sys.stderr, flush=True)
+        for index, M in [(5, 8), (5, 64)]:   # the other kernel on either side of the crossover
+            other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
+            r = measure(wq, torch, index, M, min(args.steps, 100), min(args.warmup, 10), kernel=other)
+            rows.append(r)
+            print(f"# {r}", file=sys.stderr, flush=True)
+        for index in (2, 5):
+            o = measure_offline(wq, torch, index)
+            offline.append(o)
+            print(f"# offline {o}", file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu else cpu_baseline()
+    us = head["us_per_launch"]
+    line = {
+        "metric": "W4A16 linear: decode GB/s (% HBM peak), prefill TFLOP/s (% MFMA peak)",
+        "value": round(head["GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV, Llama-7B MLP up-proj: x fp16 [1,4096], W [11008,4096] "
+                               "INT4 asym g128 packed 8/uint32, y fp16",
+                   "M": 1, "N": 11008, "K": 4096, "group": 128, "kernel": head["kernel"],
+                   "rotated_sets": head["rotated_sets"]},
+        "roofline": {"bound": "hbm", "achieved": round(head["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["hbm_frac"], 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "workloads": rows,
+        "offline": offline,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * wq.h - C ABI of the MI355X (gfx950) W4A16 group-quantized linear layer.
+ *
+ * The layer computes y = x . dequant(Wq)^T + W_sparse . x, the dense-and-sparse
+ * product of the SqueezeLLM explainer (sections 2.2-2.3: W = W_dense + W_sparse,
+ * W x = W_dense x + W_sparse x), where the dense part holds asymmetric INT4
+ * round-to-nearest codes with one fp16 scale and zero-point per group of 128
+ * input channels (the "W4A16 g128" rows of the DeepCompressor README perplexity
+ * table; RTN as the calibration-free baseline in the AWQ paper, section 2), packed
+ * eight codes per 32-bit word and dequantized on the fly inside the product (AWQ
+ * paper, section 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates or frees memory, keeps no state between calls, launches its
+ *    kernels on `stream` (a hipStream_t; NULL = the default stream) and never
+ *    synchronizes: results are ready when work queued after them on `stream`
+ *    runs. Calls that share output or workspace buffers must not overlap.
+ *  - fp16 values travel as uint16_t bit patterns. All arrays are row-major and
+ *    contiguous.
+ *  - Every argument is validated on the host BEFORE any HIP call; a failed
+ *    validation returns a negative wq_status and launches nothing. A failed
+ *    kernel launch returns WQ_ERR_HIP (hipGetLastError() then holds the cause).
+ *  - Preconditions the device does not check: inputs are finite; a group's
+ *    range (max - min) is at most 15 * 65504 and every |w| of a sparse entry at
+ *    most 65504, so scales and sparse values fit fp16; INT4 codes are <= 15.
+ *  - Integer sizes: 1 <= N, 1 <= M, K a positive multiple of 128, N*K < 2^31.
+ *  - Alignment: W, x, codes and packed must be 16-byte aligned (WQ_ERR_ALIGN).
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WQ_OK = 0,
+  WQ_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  WQ_ERR_SHAPE = -2,       /* a size is out of range or inconsistent            */
+  WQ_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned                  */
+  WQ_ERR_UNSUPPORTED = -4, /* group size other than 128, unknown dtype / kernel */
+  WQ_ERR_HIP = -5,         /* a kernel launch failed                            */
+  WQ_ERR_WORKSPACE = -6    /* workspace missing or smaller than required        */
+} wq_status;
+
+typedef enum { WQ_F16 = 0, WQ_F32 = 1 } wq_dtype;
+
+/* Kernel choice for the linear entry points. AUTO uses the decode GEMV for
+ * M <= 16 and the MFMA GEMM above; the others force one kernel at any M. */
+typedef enum { WQ_KERNEL_AUTO = 0, WQ_KERNEL_GEMV = 1, WQ_KERNEL_GEMM = 2 } wq_kernel;
+
+/* Bytes of device workspace wq_quantize_rtn needs (0 when sparse_k == 0).
+ * Returns 0 for invalid sizes as well; wq_quantize_rtn reports those. */
+size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k);
+
+/*
+ * wq_quantize_rtn - offline dense-and-sparse split plus RTN group quantization.
+ *
+ *  W        [N, K] float32, the weights (output channel n, input channel k).
+ *  group    must be 128 (WQ_ERR_UNSUPPORTED otherwise).
+ *  sparse_k number of entries moved to the sparse fp16 part, 0 <= sparse_k <= N*K.
+ *           They are the sparse_k entries of largest |w| (ties: lower flat index
+ *           n*K + k first); the SqueezeLLM explainer (section 2.2) keeps such a
+ *           small fraction (0.05 % / 0.45 %) of the weights in fp16, chosen there by
+ *           a Hessian sensitivity that needs calibration data, here by magnitude.
+ *           The dense part is W with those entries set to +0.
+ *  codes    [N, K] uint8 out: q = clamp(rint(w / s) + z, 0, 15) for the dense part.
+ *  scales   [N, K/128] fp16 out: s = fp16(max(fl32(fl32(max - min) / 15), 2^-14)).
+ *  zeros    [N, K/128] fp16 out: z = clamp(rint(-min / s), 0, 15), an integer.
+ *           (All float32 steps are IEEE, correctly rounded, half-to-even.)
+ *  row_ptr  [N+1] int32 out, col [sparse_k] int32 out, val [sparse_k] fp16 out:
+ *           the sparse part in CSR, rows = output channels, columns ascending.
+ *           Required when sparse_k > 0; when sparse_k == 0 they may be NULL, and a
+ *           non-NULL row_ptr is filled with zeros.
+ *  workspace device scratch of at least wq_quantize_workspace_bytes(N, K, sparse_k)
+ *           bytes (may be NULL when that is 0). Its contents on entry do not matter.
+ */
+int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t sparse_k,
+                    uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                    int32_t* row_ptr, int32_t* col, uint16_t* val,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wq_pack - 4-bit packing (AWQ paper, section 1): eight consecutive codes along K
+ * per 32-bit word, code k = 8t + i in bits [4i, 4i + 4) of word t.
+ *  codes  [N, K] uint8 in (only the low 4 bits of each byte are used).
+ *  packed [N, K/8] uint32 out.
+ */
+int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* stream);
+
+/* Bytes of device workspace the linear entry points need for these sizes.
+ * The current kernels need none (0); pass it anyway for forward compatibility. */
+size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * wq_linear - y = x . dequant(packed, scales, zeros)^T with on-the-fly
+ * dequantization w_hat[n, k] = (q[n, k] - z[n, k/128]) * s[n, k/128].
+ *  x       [M, K] fp16 activations.
+ *  packed  [N, K/8] uint32 codes as written by wq_pack.
+ *  scales, zeros [N, K/128] fp16 as written by wq_quantize_rtn.
+ *  y       [M, N] out, fp16 (y_dtype = WQ_F16, one rounding of the fp32
+ *          accumulator) or float32 (WQ_F32). Accumulation is fp32.
+ *  Results are deterministic: no atomics, fixed reduction order.
+ */
+int wq_linear(const uint16_t* x, int64_t M, int64_t K,
+              const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+              int64_t N, int32_t group, void* y, int32_t y_dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wq_linear_sparse - wq_linear plus the sparse term W_sparse . x (SqueezeLLM
+ * explainer, section 2.3), added to the same fp32 accumulators before the one
+ * store of y:  y[m, n] += sum over CSR entries e of row n of val[e] * x[m, col[e]].
+ *  row_ptr [N+1], col [nnz] int32 and val [nnz] fp16 as written by
+ *  wq_quantize_rtn (row_ptr[0] == 0, row_ptr[N] == nnz, columns in [0, K)).
+ *  nnz == 0 is valid and equals wq_linear (col / val may then be NULL).
+ */
+int wq_linear_sparse(const uint16_t* x, int64_t M, int64_t K,
+                     const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                     int64_t N, int32_t group,
+                     const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
+                     void* y, int32_t y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wq_linear_sparse_kernel - wq_linear_sparse with an explicit kernel choice
+ * (wq_kernel), used to measure both kernels on either side of the M crossover.
+ * row_ptr may be NULL (then nnz must be 0): this is the dense product.
+ */
+int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K,
+                            const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                            int64_t N, int32_t group,
+                            const int32_t* row_ptr, const int32_t* col, const uint16_t* val,
+                            int64_t nnz, void* y, int32_t y_dtype, int32_t kernel,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* The kernel WQ_KERNEL_AUTO picks for M rows (WQ_KERNEL_GEMV or WQ_KERNEL_GEMM). */
+int wq_auto_kernel(int64_t M, int64_t N, int64_t K);
+
+/* A static, NUL-terminated description of a wq_status value. */
+const char* wq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

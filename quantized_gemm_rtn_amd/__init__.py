@@ -1,0 +1,179 @@
+"""Python binding of libwq.so, the gfx950 W4A16 group-quantized linear.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind include/wq.h.  PyTorch provides device memory and the current
+stream.  There is no fallback: if the library is missing, every call raises.
+
+Entry points (the same names as the C ABI, without the ``wq_`` prefix):
+
+* ``quantize_rtn(W, sparse_k)``  split + RTN INT4 group quantization
+* ``pack(codes)``                eight codes per 32-bit word
+* ``linear(x, packed, scales, zeros)``
+* ``linear_sparse(x, packed, scales, zeros, row_ptr, col, val)``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libwq.so")
+GROUP = 128
+
+WQ_OK = 0
+STATUS = {0: "WQ_OK", -1: "WQ_ERR_NULL", -2: "WQ_ERR_SHAPE", -3: "WQ_ERR_ALIGN",
+          -4: "WQ_ERR_UNSUPPORTED", -5: "WQ_ERR_HIP", -6: "WQ_ERR_WORKSPACE"}
+KERNELS = {"auto": 0, "gemv": 1, "gemm": 2}
+
+# name -> (restype, argtypes) for every symbol declared in include/wq.h
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = {
+    "wq_quantize_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "wq_quantize_rtn": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "wq_pack": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
+    "wq_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "wq_linear": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "wq_linear_sparse": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
+                                        _vp, _i32, _vp, _sz, _vp]),
+    "wq_linear_sparse_kernel": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
+                                               _vp, _i32, _i32, _vp, _sz, _vp]),
+    "wq_auto_kernel": (ctypes.c_int, [_i64, _i64, _i64]),
+    "wq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+class WQError(RuntimeError):
+    def __init__(self, fn, status, lib):
+        msg = lib.wq_status_string(status).decode() if lib is not None else ""
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libwq.so (built by ``python -m quantized_gemm_rtn_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m quantized_gemm_rtn_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(fn, rc):
+    if rc != WQ_OK:
+        raise WQError(fn, rc, _lib)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_workspace_bytes(N, K, sparse_k):
+    return int(load().wq_quantize_workspace_bytes(N, K, sparse_k))
+
+
+def quantize_rtn(W, sparse_k: int = 0, group: int = GROUP, workspace=None):
+    """Dense-and-sparse split and RTN INT4 quantization of ``W`` (float32 [N, K]).
+
+    Returns a dict with ``codes`` uint8 [N, K], ``scales``/``zeros`` float16
+    [N, K/128], and the sparse part ``row_ptr`` int32 [N+1], ``col`` int32
+    [sparse_k], ``val`` float16 [sparse_k]."""
+    import torch
+    lib = load()
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    dev = W.device
+    G = K // group if group else 0
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)
+    zeros = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)
+    row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    col = torch.empty(max(sparse_k, 1), dtype=torch.int32, device=dev)
+    val = torch.empty(max(sparse_k, 1), dtype=torch.float16, device=dev)
+    nbytes = int(lib.wq_quantize_workspace_bytes(N, K, sparse_k))
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rc = lib.wq_quantize_rtn(_p(W), N, K, group, sparse_k, _p(codes), _p(scales), _p(zeros), _p(row_ptr),
+                             _p(col), _p(val), _p(workspace), nbytes if workspace is not None else 0, _stream(W))
+    _check("wq_quantize_rtn", rc)
+    return dict(codes=codes, scales=scales[:, :G], zeros=zeros[:, :G], row_ptr=row_ptr,
+                col=col[:sparse_k], val=val[:sparse_k])
+
+
+def pack(codes):
+    """Eight INT4 codes per 32-bit word (returned as int32 bit patterns)."""
+    import torch
+    lib = load()
+    _need(codes, torch.uint8, "codes")
+    N, K = codes.shape
+    packed = torch.empty((N, K // 8), dtype=torch.int32, device=codes.device)
+    _check("wq_pack", lib.wq_pack(_p(codes), N, K, _p(packed), _stream(codes)))
+    return packed
+
+
+def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, out_dtype=None,
+                  kernel: str = "auto", out=None, group: int = GROUP):
+    """y = x . dequant(packed, scales, zeros)^T (+ W_sparse x when CSR is given)."""
+    import torch
+    lib = load()
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    _need(x, torch.float16, "x")
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.float16, "zeros")
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 8 != K or scales.shape != (N, K // group) or zeros.shape != scales.shape:
+        raise ValueError("inconsistent shapes")
+    nnz = 0
+    if row_ptr is not None:
+        _need(row_ptr, torch.int32, "row_ptr")
+        if row_ptr.numel() != N + 1:
+            raise ValueError("row_ptr must have N+1 entries")
+        nnz = int(col.numel()) if col is not None else 0
+        if nnz:
+            _need(col, torch.int32, "col")
+            _need(val, torch.float16, "val")
+    if out_dtype not in (torch.float16, torch.float32):
+        raise TypeError("out_dtype must be float16 or float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    y_dtype = 1 if out_dtype == torch.float32 else 0
+    rc = lib.wq_linear_sparse_kernel(_p(x), M, K, _p(packed), _p(scales), _p(zeros), N, group,
+                                     _p(row_ptr), _p(col) if nnz else None, _p(val) if nnz else None, nnz,
+                                     _p(out), y_dtype, KERNELS[kernel], None, 0, _stream(x))
+    _check("wq_linear_sparse_kernel", rc)
+    return out
+
+
+def linear(x, packed, scales, zeros, out_dtype=None, kernel: str = "auto", out=None, group: int = GROUP):
+    return linear_sparse(x, packed, scales, zeros, None, None, None, out_dtype, kernel, out, group)
+
+
+def auto_kernel(M, N, K) -> str:
+    k = int(load().wq_auto_kernel(M, N, K))
+    return {1: "gemv", 2: "gemm"}[k]

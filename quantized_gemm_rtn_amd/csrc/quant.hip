@@ -1,0 +1,101 @@
+// RTN group quantizer and INT4 packer for gfx950.
+//
+// Quantizer (asymmetric INT4, one scale and zero-point per 128 input channels;
+// round-to-nearest is the calibration-free baseline of the AWQ paper, section 2,
+// and the LLM Compressor article's FAQ; "W4A16 g128" in the DeepCompressor README
+// perplexity table): per group, mn/mx -> s = fp16(max(fl32(mx - mn) / 15, 2^-14)),
+// z = clamp(rint(-mn / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15).
+//
+// The codes are integers decided by float32 arithmetic, so this file must round
+// exactly like the definition: IEEE float32 division correctly rounded
+// (__fdiv_rn), rintf = round half to even (v_rndne_f32), fp16 conversion to
+// nearest even, and no contraction (the translation unit is built with
+// -ffp-contract=off; nothing here would contract anyway).
+//
+// The quantizer is HBM-bound (4 B read + 1 B written per weight); one wave owns
+// one group of 128 weights at a time: a 512-byte coalesced load (two floats per
+// lane), a butterfly min/max across the wave, and a 128-byte store of codes.
+#include "wq_device.h"
+#include "wq_launch.h"
+
+namespace wq {
+
+__global__ void __launch_bounds__(256)
+rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ mask, int64_t N, int64_t K,
+                    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                    uint16_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t G = K / kGroup;
+  const int64_t total = N * G;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  for (int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); gid < total; gid += stride) {
+    const int64_t n = gid / G;
+    const int64_t g = gid - n * G;
+    const int64_t off = n * K + g * kGroup + 2 * lane;
+    float2 v = *reinterpret_cast<const float2*>(W + off);
+    if (mask != nullptr) {
+      // entries moved to the sparse part count as +0 in the dense part
+      const uint32_t mw = mask[off >> 5];
+      const uint32_t b = (uint32_t)(off & 31);
+      if ((mw >> b) & 1u) v.x = 0.0f;
+      if ((mw >> (b + 1)) & 1u) v.y = 0.0f;
+    }
+    float mn = fminf(v.x, v.y);
+    float mx = fmaxf(v.x, v.y);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o));
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    float d = __fdiv_rn(mx - mn, 15.0f);
+    d = fmaxf(d, 0x1p-14f);
+    const f16 s16 = (f16)d;
+    const float s = (float)s16;
+    float zf = rintf(__fdiv_rn(-mn, s));
+    zf = fminf(fmaxf(zf, 0.0f), 15.0f);
+    const int zi = (int)zf;  // an integer, so a -0 never reaches the stored fp16
+    float t0 = rintf(__fdiv_rn(v.x, s)) + (float)zi;
+    float t1 = rintf(__fdiv_rn(v.y, s)) + (float)zi;
+    t0 = fminf(fmaxf(t0, 0.0f), 15.0f);
+    t1 = fminf(fmaxf(t1, 0.0f), 15.0f);
+    const uint32_t q0 = (uint32_t)t0, q1 = (uint32_t)t1;
+    *reinterpret_cast<uint16_t*>(codes + off) = (uint16_t)(q0 | (q1 << 8));
+    if (lane == 0) {
+      scales[gid] = __builtin_bit_cast(uint16_t, s16);
+      zeros[gid] = __builtin_bit_cast(uint16_t, (f16)(float)zi);
+    }
+  }
+}
+
+// Eight codes (one per byte, low nibble used) -> one word, code i in bits [4i, 4i+4).
+__global__ void __launch_bounds__(256)
+pack_kernel(const uint8_t* __restrict__ codes, int64_t nwords, uint32_t* __restrict__ packed) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) {
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + 8 * i);
+    const uint32_t lo = c.x & 0x0F0F0F0Fu, hi = c.y & 0x0F0F0F0Fu;
+    packed[i] = (lo & 0xFu) | ((lo >> 4) & 0xF0u) | ((lo >> 8) & 0xF00u) | ((lo >> 12) & 0xF000u) |
+                ((hi & 0xFu) << 16) | ((hi << 12) & 0xF00000u) | ((hi << 8) & 0xF000000u) |
+                ((hi << 4) & 0xF0000000u);
+  }
+}
+
+static int64_t clamp_blocks(int64_t want) { return want < 1 ? 1 : (want > 65536 ? 65536 : want); }
+
+hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, uint8_t* codes,
+                           uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+  const int64_t groups = N * (K / kGroup);
+  const int64_t blocks = clamp_blocks((groups + 3) / 4);
+  hipLaunchKernelGGL(rtn_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
+                     codes, scales, zeros);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream) {
+  const int64_t nwords = N * (K / 8);
+  const int64_t blocks = clamp_blocks((nwords + 255) / 256);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, nwords, packed);
+  return hipGetLastError();
+}
+
+}  // namespace wq

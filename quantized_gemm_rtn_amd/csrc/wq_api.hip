@@ -1,0 +1,149 @@
+// C ABI of the W4A16 group-quantized linear (declared in include/wq.h).
+//
+// Every entry point validates all of its arguments on the host before it makes
+// any HIP call, so a bad call returns a negative status and launches nothing
+// (and the validation is testable on a machine without a GPU).
+#include "../../include/wq.h"
+#include "wq_launch.h"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int64_t kMax32 = (int64_t)1 << 31;  // element counts must stay below 2^31
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int check_linear_args(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
+                      const uint16_t* zeros, int64_t N, int32_t group, const int32_t* row_ptr,
+                      const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int32_t y_dtype,
+                      int32_t kernel) {
+  if (!x || !packed || !scales || !zeros || !y) return WQ_ERR_NULL;
+  if (row_ptr == nullptr && nnz != 0) return WQ_ERR_NULL;
+  if (nnz > 0 && (!col || !val)) return WQ_ERR_NULL;
+  if (group != kGroup) return WQ_ERR_UNSUPPORTED;
+  if (y_dtype != WQ_F16 && y_dtype != WQ_F32) return WQ_ERR_UNSUPPORTED;
+  if (kernel != WQ_KERNEL_AUTO && kernel != WQ_KERNEL_GEMV && kernel != WQ_KERNEL_GEMM) return WQ_ERR_UNSUPPORTED;
+  if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) return WQ_ERR_SHAPE;
+  if (nnz < 0 || nnz >= kMax32) return WQ_ERR_SHAPE;
+  if (N >= kMax32 / K || M >= kMax32 / K || M >= kMax32 / N) return WQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(y, 4))
+    return WQ_ERR_ALIGN;
+  if ((row_ptr && !aligned(row_ptr, 4)) || (col && !aligned(col, 4)) || (val && !aligned(val, 2)))
+    return WQ_ERR_ALIGN;
+  return WQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wq_status_string(int status) {
+  switch (status) {
+    case WQ_OK: return "ok";
+    case WQ_ERR_NULL: return "a required pointer is NULL";
+    case WQ_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case WQ_ERR_ALIGN: return "a pointer is not sufficiently aligned";
+    case WQ_ERR_UNSUPPORTED: return "unsupported group size, dtype or kernel choice";
+    case WQ_ERR_HIP: return "a HIP kernel launch failed";
+    case WQ_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k) {
+  if (N < 1 || K < kGroup || K % kGroup != 0 || N >= kMax32 / K) return 0;
+  if (sparse_k <= 0) return 0;
+  return wq::split_workspace_bytes(N, K);
+}
+
+int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t sparse_k, uint8_t* codes,
+                    uint16_t* scales, uint16_t* zeros, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W || !codes || !scales || !zeros) return WQ_ERR_NULL;
+  if (sparse_k > 0 && (!row_ptr || !col || !val)) return WQ_ERR_NULL;
+  if (group != kGroup) return WQ_ERR_UNSUPPORTED;
+  if (N < 1 || K < kGroup || K % kGroup != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
+  if (sparse_k < 0 || sparse_k > N * K) return WQ_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2)) return WQ_ERR_ALIGN;
+  if ((row_ptr && !aligned(row_ptr, 4)) || (col && !aligned(col, 4)) || (val && !aligned(val, 2)))
+    return WQ_ERR_ALIGN;
+  if (sparse_k > 0) {
+    const size_t need = wq::split_workspace_bytes(N, K);
+    if (!workspace || workspace_bytes < need) return WQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
+  }
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = hipSuccess;
+  if (sparse_k > 0) {
+    const wq::SplitWorkspace ws = wq::split_workspace_carve(workspace, N, K);
+    e = wq::launch_split(W, N, K, sparse_k, row_ptr, col, val, ws, s);
+    if (e == hipSuccess) e = wq::launch_quantize(W, ws.mask, N, K, codes, scales, zeros, s);
+  } else {
+    if (row_ptr) e = wq::launch_fill_zero_i32(row_ptr, N + 1, s);
+    if (e == hipSuccess) e = wq::launch_quantize(W, nullptr, N, K, codes, scales, zeros, s);
+  }
+  return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+}
+
+int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* stream) {
+  if (!codes || !packed) return WQ_ERR_NULL;
+  if (N < 1 || K < 8 || K % 8 != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(packed, 16)) return WQ_ERR_ALIGN;
+  return wq::launch_pack(codes, N, K, packed, as_stream(stream)) == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+}
+
+size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+int wq_auto_kernel(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return M <= 16 ? WQ_KERNEL_GEMV : WQ_KERNEL_GEMM;
+}
+
+int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
+                            const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                            const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
+                            void* y, int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                                   kernel);
+  if (rc != WQ_OK) return rc;
+  if (kernel == WQ_KERNEL_AUTO) kernel = wq_auto_kernel(M, N, K);
+  const int y_f32 = y_dtype == WQ_F32;
+  const int32_t* rp = nnz > 0 ? row_ptr : nullptr;  // nnz == 0: the dense product
+  hipError_t e;
+  if (kernel == WQ_KERNEL_GEMV)
+    e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, as_stream(stream));
+  else
+    e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, as_stream(stream));
+  return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+}
+
+int wq_linear_sparse(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
+                     const uint16_t* zeros, int64_t N, int32_t group, const int32_t* row_ptr, const int32_t* col,
+                     const uint16_t* val, int64_t nnz, void* y, int32_t y_dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!row_ptr) return WQ_ERR_NULL;
+  return wq_linear_sparse_kernel(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                                 WQ_KERNEL_AUTO, workspace, workspace_bytes, stream);
+}
+
+int wq_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
+              const uint16_t* zeros, int64_t N, int32_t group, void* y, int32_t y_dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return wq_linear_sparse_kernel(x, M, K, packed, scales, zeros, N, group, nullptr, nullptr, nullptr, 0, y,
+                                 y_dtype, WQ_KERNEL_AUTO, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

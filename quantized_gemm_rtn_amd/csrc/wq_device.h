@@ -1,0 +1,80 @@
+// Device-side helpers shared by the gfx950 kernels of the W4A16 linear.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 128;
+
+// One CDNA4 matrix-core step: a 16x32 fp16 tile times a 32x16 fp16 tile added to
+// a 16x16 fp32 tile. Lane l supplies A[l%16][8*(l/16) + j] and B[8*(l/16) + j][l%16]
+// for j = 0..7 and receives D[4*(l/16) + i][l%16] for i = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Dequantization order inside one 32-bit word.
+//
+// fp16 0x6400 is 1024.0 and its ten mantissa bits have weight 1, so OR-ing a
+// 4-bit code q into the low mantissa gives exactly 1024 + q. Masking a word with
+// 0x000F000F therefore yields two halves at once: codes 0 and 4, then (after
+// shifting by 4, 8, 12) codes 1/5, 2/6, 3/7. The eight values of a word thus come
+// out in the order 0,4,1,5,2,6,3,7. A contraction over K does not care about the
+// order inside a chunk of eight, as long as the activations are fed in the same
+// order: perm_x8 reorders eight consecutive activations to match.
+__device__ __forceinline__ uint4 codes_biased(uint32_t w) {
+  uint4 r;
+  r.x = (w & 0x000F000Fu) | 0x64006400u;
+  r.y = ((w >> 4) & 0x000F000Fu) | 0x64006400u;
+  r.z = ((w >> 8) & 0x000F000Fu) | 0x64006400u;
+  r.w = ((w >> 12) & 0x000F000Fu) | 0x64006400u;
+  return r;
+}
+
+// (q - z) for the eight codes of a word, exact in fp16 (|q - z| <= 15):
+// (1024 + q) - (1024 + z) with both operands exact.
+__device__ __forceinline__ f16x8 codes_minus_zero(uint32_t w, f16x2 bias) {
+  uint4 b = codes_biased(w);
+  f16x2 a0 = as_f16x2(b.x) - bias, a1 = as_f16x2(b.y) - bias;
+  f16x2 a2 = as_f16x2(b.z) - bias, a3 = as_f16x2(b.w) - bias;
+  uint4 o = {as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3)};
+  return as_f16x8(o);
+}
+
+// fp16((q - z) * s): one rounding of the exact difference times the scale.
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, f16x2 bias, f16x2 s) {
+  uint4 b = codes_biased(w);
+  f16x2 a0 = (as_f16x2(b.x) - bias) * s, a1 = (as_f16x2(b.y) - bias) * s;
+  f16x2 a2 = (as_f16x2(b.z) - bias) * s, a3 = (as_f16x2(b.w) - bias) * s;
+  uint4 o = {as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3)};
+  return o;
+}
+
+// Eight consecutive fp16 values x0..x7 (two per dword) reordered to
+// x0,x4,x1,x5,x2,x6,x3,x7, the order codes_biased produces.
+__device__ __forceinline__ uint4 perm_x8(uint4 v) {
+  uint4 o;
+  o.x = (v.x & 0xFFFFu) | (v.z << 16);
+  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+  o.z = (v.y & 0xFFFFu) | (v.w << 16);
+  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  return o;
+}
+
+// Slot of element j (0..7) of a chunk of eight after perm_x8.
+__device__ __forceinline__ int perm_slot(int j) { return ((j & 3) << 1) | (j >> 2); }
+
+__device__ __forceinline__ f16 bits_to_f16(uint16_t b) { return __builtin_bit_cast(f16, b); }
+
+}  // namespace wq

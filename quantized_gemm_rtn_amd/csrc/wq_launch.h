@@ -1,0 +1,37 @@
+// Host-side launchers of the gfx950 kernels (internal; the public ABI is include/wq.h).
+// Each returns the hipError_t of its launches; arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wq {
+
+// Workspace carved up by the outlier split.
+struct SplitWorkspace {
+  uint32_t* hist;     // [2048] radix histogram
+  uint32_t* state;    // [16]   select state: prefix, prefix mask, k remaining, count above
+  uint32_t* cnt_gt;   // [N]    per row: keys above the threshold
+  uint32_t* cnt_eq;   // [N]    per row: keys equal to the threshold
+  uint32_t* take_eq;  // [N]    per row: equal keys that are selected
+  uint32_t* mask;     // [N*K/32] selection bitmap
+};
+size_t split_workspace_bytes(int64_t N, int64_t K);
+SplitWorkspace split_workspace_carve(void* base, int64_t N, int64_t K);
+
+hipError_t launch_split(const float* W, int64_t N, int64_t K, int64_t sparse_k, int32_t* row_ptr,
+                        int32_t* col, uint16_t* val, const SplitWorkspace& ws, hipStream_t stream);
+hipError_t launch_fill_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
+hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, uint8_t* codes,
+                           uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream);
+
+hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
+                       const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
+                       const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream);
+hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
+                       const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
+                       const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream);
+
+}  // namespace wq

@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/wq.h declares, and rejects bad arguments on the host before any HIP call
+(the fake device addresses below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gemm_rtn_amd as wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+A = ctypes.c_void_p(0x7F0000000000)      # 16-byte aligned fake device address
+A2 = ctypes.c_void_p(0x7F0000100000)
+A3 = ctypes.c_void_p(0x7F0000200000)
+A4 = ctypes.c_void_p(0x7F0000300000)
+A5 = ctypes.c_void_p(0x7F0000400000)
+MIS = ctypes.c_void_p(0x7F0000000008)    # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(wq.LIB_PATH):
+        import quantized_gemm_rtn_amd.build as b
+        b.build()
+    return wq.load()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree(lib):
+    names = header_functions()
+    assert "wq_quantize_rtn" in names and "wq_pack" in names
+    assert "wq_linear" in names and "wq_linear_sparse" in names
+    assert sorted(wq.SIGNATURES) == names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(wq.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        s = lib.wq_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.wq_status_string(-99).decode() == "unknown status"
+
+
+def test_auto_kernel(lib):
+    assert lib.wq_auto_kernel(1, 11008, 4096) == 1
+    assert lib.wq_auto_kernel(16, 4096, 4096) == 1
+    assert lib.wq_auto_kernel(17, 4096, 4096) == 2
+    assert lib.wq_auto_kernel(2048, 14336, 4096) == 2
+
+
+def test_workspace_sizes(lib):
+    assert lib.wq_quantize_workspace_bytes(64, 256, 0) == 0
+    b = lib.wq_quantize_workspace_bytes(4096, 4096, 75497)
+    assert b >= 4096 * 4096 // 8 + 3 * 4096 * 4 + 2048 * 4
+    assert lib.wq_quantize_workspace_bytes(64, 100, 5) == 0      # invalid K
+    assert lib.wq_linear_workspace_bytes(512, 8192, 28672) == 0
+
+
+def linear(lib, x=A, M=1, K=256, packed=A2, scales=A3, zeros=A4, N=64, group=128, row_ptr=None, col=None,
+           val=None, nnz=0, y=A5, y_dtype=0, kernel=0):
+    return lib.wq_linear_sparse_kernel(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y,
+                                       y_dtype, kernel, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), -1), (dict(packed=None), -1), (dict(scales=None), -1), (dict(zeros=None), -1),
+    (dict(y=None), -1), (dict(nnz=5, row_ptr=None), -1), (dict(row_ptr=A, nnz=3, col=None, val=A2), -1),
+    (dict(row_ptr=A, nnz=3, col=A2, val=None), -1),
+    (dict(group=64), -4), (dict(y_dtype=2), -4), (dict(kernel=3), -4),
+    (dict(M=0), -2), (dict(N=0), -2), (dict(K=0), -2), (dict(K=100), -2), (dict(K=64), -2),
+    (dict(nnz=-1, row_ptr=A), -2), (dict(M=1 << 20, K=4096), -2), (dict(N=1 << 20, K=4096), -2),
+    (dict(x=MIS), -3), (dict(packed=MIS), -3), (dict(scales=ctypes.c_void_p(0x7F0000000001)), -3),
+    (dict(y=ctypes.c_void_p(0x7F0000000002)), -3),
+])
+def test_linear_validation(lib, kw, status):
+    assert linear(lib, **kw) == status
+
+
+def test_linear_wrappers_validate(lib):
+    assert lib.wq_linear(None, 1, 256, A2, A3, A4, 64, 128, A5, 0, None, 0, None) == -1
+    assert lib.wq_linear(A, 1, 256, A2, A3, A4, 64, 32, A5, 0, None, 0, None) == -4
+    # wq_linear_sparse requires row_ptr
+    assert lib.wq_linear_sparse(A, 1, 256, A2, A3, A4, 64, 128, None, None, None, 0, A5, 0, None, 0, None) == -1
+
+
+def quant(lib, W=A, N=8, K=256, group=128, sparse_k=0, codes=A2, scales=A3, zeros=A4, row_ptr=None, col=None,
+          val=None, ws=None, ws_bytes=0):
+    return lib.wq_quantize_rtn(W, N, K, group, sparse_k, codes, scales, zeros, row_ptr, col, val, ws, ws_bytes,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), -1), (dict(codes=None), -1), (dict(scales=None), -1), (dict(zeros=None), -1),
+    (dict(sparse_k=3), -1), (dict(sparse_k=3, row_ptr=A, col=A, val=None), -1),
+    (dict(group=256), -4), (dict(K=200), -2), (dict(N=0), -2), (dict(sparse_k=-1), -2),
+    (dict(sparse_k=8 * 256 + 1, row_ptr=A, col=A, val=A), -2),
+    (dict(W=MIS), -3), (dict(codes=MIS), -3),
+    (dict(sparse_k=3, row_ptr=A, col=A, val=A), -6),
+    (dict(sparse_k=3, row_ptr=A, col=A, val=A, ws=A5, ws_bytes=16), -6),
+])
+def test_quantize_validation(lib, kw, status):
+    assert quant(lib, **kw) == status
+
+
+def test_pack_validation(lib):
+    assert lib.wq_pack(None, 4, 64, A2, None) == -1
+    assert lib.wq_pack(A, 4, 12, A2, None) == -2
+    assert lib.wq_pack(A, 0, 64, A2, None) == -2
+    assert lib.wq_pack(MIS, 4, 64, A2, None) == -3
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(wq, "_lib", None)
+    monkeypatch.setattr(wq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        wq.load()

@@ -1,0 +1,142 @@
+"""Parity of the GPU decode GEMV and prefill GEMM (with the fused sparse term)
+with the float64 oracle: ||y - y_ref||_inf <= 5e-3 ||y_ref||_inf, bit-identical
+fp32 results on the integer-exact case, and run-to-run determinism."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_cases import layer_to_dev, oracle_layer, run_linear, sample_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = oracle.TOL
+
+
+def _full_check(wq, torch, L, x, kernel, out_dtype=None, sparse=True, label=""):
+    D = layer_to_dev(L, torch)
+    xd = to_dev(x, torch)
+    say(f"[linear] {label} M={x.shape[0]} N,K={L['q'].shape} kernel={kernel}")
+    y = run_linear(wq, xd, D, kernel=kernel, out_dtype=out_dtype, sparse=sparse)
+    torch.cuda.synchronize()
+    if sparse:
+        ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    else:
+        ref = oracle.linear_ref(x, L["q"], L["s"], L["z"])
+    err = oracle.rel_err_inf(y.float().cpu().numpy(), ref)
+    say(f"    rel err {err:.3e}")
+    assert err <= TOL, err
+    return y
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+@pytest.mark.parametrize("kernel", ["auto", "gemm"])
+def test_small_configs_full(gpu_lib, index, kernel):
+    import torch
+    L = oracle_layer(index)
+    _, x, _ = workloads.make(index)
+    _full_check(gpu_lib, torch, L, x, kernel, label=f"config {index}")
+
+
+def _sampled_check(wq, torch, L, x, kernel, rows, label):
+    D = layer_to_dev(L, torch)
+    xd = to_dev(x, torch)
+    say(f"[linear] {label} M={x.shape[0]} N,K={L['q'].shape} kernel={kernel} sampled={len(rows)}")
+    y = run_linear(wq, xd, D, kernel=kernel)
+    torch.cuda.synchronize()
+    ys = y.float().cpu().numpy()
+    assert np.isfinite(ys).all()
+    ref = oracle.linear_rows(x, L["packed"], L["s"], L["z"], rows, L["row_ptr"], L["col"], L["val"])
+    err = oracle.rel_err_inf(ys[:, rows], ref)
+    say(f"    rel err {err:.3e}")
+    assert err <= TOL, err
+
+
+def test_config4_prefill_sampled(gpu_lib):
+    import torch
+    L = oracle_layer(4)
+    _, x, _ = workloads.make(4)
+    _sampled_check(gpu_lib, torch, L, x, "auto", sample_rows(L["q"].shape[0], 96, 4), "config 4")
+
+
+@pytest.mark.parametrize("M", [1, 8, 64, 512])
+def test_config5_sweep_sampled(gpu_lib, M):
+    import torch
+    L = oracle_layer(5)
+    _, x, _ = workloads.make(5, M=M)
+    _sampled_check(gpu_lib, torch, L, x, "auto", sample_rows(L["q"].shape[0], 96, 5 + M), f"config 5")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 15, 16, 17, 31, 33, 64, 65, 130])
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+def test_ragged_shapes(gpu_lib, M, kernel):
+    import torch
+    N, K = 300, 640
+    W = workloads.random_weights(100 + M, N, K)
+    L = oracle.quantize_layer(W, 700)
+    x = workloads.random_x(200 + M, M, K)
+    _full_check(gpu_lib, torch, L, x, kernel, label="ragged")
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 128, 1), (17, 128, 5), (130, 256, 70), (16, 1152, 16), (257, 384, 129)])
+@pytest.mark.parametrize("kernel", ["auto", "gemv", "gemm"])
+def test_edge_shapes(gpu_lib, N, K, M, kernel):
+    import torch
+    W = workloads.random_weights(N * 7 + K, N, K)
+    L = oracle.quantize_layer(W, max(1, N * K // 200))
+    x = workloads.random_x(M + N, M, K)
+    _full_check(gpu_lib, torch, L, x, kernel, label="edge")
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_integer_exact_fp32(gpu_lib, kernel, M):
+    """Power-of-two scales, integer zero-points, codes, activations and sparse
+    values: every partial sum is exact in fp32, so y must be bit-identical."""
+    import torch
+    N, K = 96, 1024
+    x, q, s, z, rp, col, val = workloads.integer_case(3 + M, M, N, K, nnz_per_row=5)
+    L = dict(q=q, s=s, z=z, packed=oracle.pack(q), row_ptr=rp, col=col, val=val)
+    D = layer_to_dev(L, torch)
+    say(f"[exact] kernel={kernel} M={M}")
+    y = run_linear(gpu_lib, to_dev(x, torch), D, kernel=kernel, out_dtype=torch.float32)
+    ref = oracle.linear_ref(x, q, s, z, rp, col, val)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+def test_empty_sparse_equals_dense(gpu_lib, kernel):
+    import torch
+    L = oracle_layer(1)
+    _, x, _ = workloads.make(1)
+    D = layer_to_dev(L, torch)
+    xd = to_dev(x, torch)
+    a = gpu_lib.linear(xd, D["packed"], D["scales"], D["zeros"], kernel=kernel)
+    b = gpu_lib.linear_sparse(xd, D["packed"], D["scales"], D["zeros"], D["row_ptr"], D["col"], D["val"],
+                              kernel=kernel)
+    assert L["sparse_k"] == 0 and torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "gemm"])
+def test_deterministic(gpu_lib, kernel):
+    import torch
+    L = oracle_layer(3)
+    _, x, _ = workloads.make(3)
+    D = layer_to_dev(L, torch)
+    xd = to_dev(x, torch)
+    a = run_linear(gpu_lib, xd, D, kernel=kernel, out_dtype=torch.float32)
+    b = run_linear(gpu_lib, xd, D, kernel=kernel, out_dtype=torch.float32)
+    assert torch.equal(a, b)
+
+
+def test_end_to_end_gpu_pipeline(gpu_lib):
+    """GPU quantize -> pack -> linear_sparse against the oracle pipeline."""
+    import torch
+    L = oracle_layer(3)
+    _, x, _ = workloads.make(3)
+    out = gpu_lib.quantize_rtn(to_dev(L["W"], torch), sparse_k=L["sparse_k"])
+    packed = gpu_lib.pack(out["codes"])
+    y = gpu_lib.linear_sparse(to_dev(x, torch), packed, out["scales"], out["zeros"], out["row_ptr"], out["col"],
+                              out["val"])
+    ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    assert oracle.rel_err_inf(y.float().cpu().numpy(), ref) <= TOL
