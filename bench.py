@@ -184,6 +184,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel],... "
+                    "(default: the batched-decode, prefill and 70B-sweep set)")
+    ap.add_argument("--no-offline", action="store_true", help="skip timing the offline quantizer")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer needs no collective and the build targets a single "
@@ -198,21 +201,31 @@ def main():
     wq.load()
 
     head = measure(wq, torch, 2, 1, args.steps, args.warmup)
-    print(f"# headline: {head}", file=sys.stderr, flush=True)
+    print(f"# headline 2:1 {head['kernel']} {head['us_per_launch']:.2f} us  {head['GBps']:.1f} GB/s "
+          f"({100 * head['hbm_frac']:.1f}% of HBM peak)", file=sys.stderr, flush=True)
     rows = []
     offline = []
     if not args.quick:
-        plan = [(3, 16), (4, 2048), (5, 1), (5, 8), (5, 64), (5, 512)]
-        for index, M in plan:
-            steps = max(20, min(args.steps, 100)) if M >= 512 else args.steps
-            r = measure(wq, torch, index, M, steps, min(args.warmup, 10))
+        if args.workloads:
+            plan = []
+            for item in args.workloads.split(","):
+                f = item.split(":")
+                plan.append((int(f[0]), int(f[1]), f[2] if len(f) > 2 else "auto"))
+        else:
+            plan = [(3, 16, "auto"), (4, 2048, "auto"), (5, 1, "auto"), (5, 8, "auto"), (5, 64, "auto"),
+                    (5, 512, "auto")]
+            # the other kernel on either side of the crossover
+            for M in (8, 64):
+                other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
+                plan.append((5, M, other))
+        for index, M, kern in plan:
+            steps = max(20, min(args.steps, 100)) if M >= 64 else args.steps
+            r = measure(wq, torch, index, M, steps, min(args.warmup, 10), kernel=kern)
             rows.append(r)
-            print(f"# {r}", file=sys.stderr, flush=True)
-        for index, M in [(5, 8), (5, 64)]:   # the other kernel on either side of the crossover
-            other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
-            r = measure(wq, torch, index, M, min(args.steps, 100), min(args.warmup, 10), kernel=other)
-            rows.append(r)
-            print(f"# {r}", file=sys.stderr, flush=True)
+            print(f"# {r['config']}:{r['M']} {r['kernel']:4s} {r['us_per_launch']:9.2f} us  "
+                  f"{r['GBps']:8.1f} GB/s ({100 * r['hbm_frac']:5.1f}%)  {r['TFLOPs']:7.1f} TF/s "
+                  f"({100 * r['mfma_frac']:5.1f}%)", file=sys.stderr, flush=True)
+    if not args.quick and not args.no_offline:
         for index in (2, 5):
             o = measure_offline(wq, torch, index)
             offline.append(o)

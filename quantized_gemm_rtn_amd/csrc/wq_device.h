@@ -72,6 +72,37 @@ __device__ __forceinline__ uint4 perm_x8(uint4 v) {
   return o;
 }
 
+// v_and_or_b32 with the mask in a scalar register and the OR operand in a vector
+// register: (a & mask) | b in one instruction (the compiler otherwise emits an AND
+// and an OR, since this VOP3 form takes no literal operands on gfx9).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
+  return r;
+}
+
+// fp16 0x6400 (1024.0) in both halves, materialized in a vector register.
+__device__ __forceinline__ uint32_t magic_1024x2() {
+  uint32_t r;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(r));
+  return r;
+}
+
+// Five-instruction unpacking of a word into four fp16 pairs, in the order of
+// perm_x8: (1024+q0, 1024+q4), (1024+16q1, 1024+16q5), (1024+q2, 1024+q6),
+// (1024+16q3, 1024+16q7). Codes at bits 4..7 of a half are left in place, so they
+// carry a factor 16 (still exact: 1024 + 16q < 2048); the activations they meet
+// are pre-scaled by 1/16.
+__device__ __forceinline__ uint4 codes_biased_x16(uint32_t w, uint32_t magic) {
+  const uint32_t w8 = w >> 8;
+  uint4 r;
+  r.x = and_or(w, 0x000F000Fu, magic);
+  r.y = and_or(w, 0x00F000F0u, magic);
+  r.z = and_or(w8, 0x000F000Fu, magic);
+  r.w = and_or(w8, 0x00F000F0u, magic);
+  return r;
+}
+
 // Slot of element j (0..7) of a chunk of eight after perm_x8.
 __device__ __forceinline__ int perm_slot(int j) { return ((j & 3) << 1) | (j >> 2); }
 
