@@ -93,8 +93,10 @@ int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t
  */
 int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* stream);
 
-/* Bytes of device workspace the linear entry points need for these sizes.
- * The current kernels need none (0); pass it anyway for forward compatibility. */
+/* Bytes of device workspace with which the linear entry points may split the K
+ * dimension of the prefill GEMM across blocks (fp32 partial sums, reduced in a
+ * fixed order), for shapes whose output tiles alone cannot fill the GPU. 0 when no
+ * split is planned. A call given less (or NULL) runs unsplit: same results, slower. */
 size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -105,6 +107,9 @@ size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *  scales, zeros [N, K/128] fp16 as written by wq_quantize_rtn.
  *  y       [M, N] out, fp16 (y_dtype = WQ_F16, one rounding of the fp32
  *          accumulator) or float32 (WQ_F32). Accumulation is fp32.
+ *  workspace: device scratch (16-byte aligned) of wq_linear_workspace_bytes(M, N, K)
+ *          bytes, or NULL; contents on entry do not matter. Calls sharing it must
+ *          not overlap.
  *  Results are deterministic: no atomics, fixed reduction order.
  */
 int wq_linear(const uint16_t* x, int64_t M, int64_t K,

@@ -133,9 +133,16 @@ def pack(codes):
     return packed
 
 
+def linear_workspace_bytes(M, N, K):
+    return int(load().wq_linear_workspace_bytes(M, N, K))
+
+
 def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, out_dtype=None,
-                  kernel: str = "auto", out=None, group: int = GROUP):
-    """y = x . dequant(packed, scales, zeros)^T (+ W_sparse x when CSR is given)."""
+                  kernel: str = "auto", out=None, group: int = GROUP, workspace=None):
+    """y = x . dequant(packed, scales, zeros)^T (+ W_sparse x when CSR is given).
+
+    ``workspace`` (uint8 device tensor of ``linear_workspace_bytes`` bytes) lets
+    the prefill GEMM split K; when omitted, one is allocated per call."""
     import torch
     lib = load()
     out_dtype = torch.float16 if out_dtype is None else out_dtype
@@ -163,15 +170,21 @@ def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, ou
     else:
         _need(out, out_dtype, "out")
     y_dtype = 1 if out_dtype == torch.float32 else 0
+    if workspace is None:
+        nbytes = int(lib.wq_linear_workspace_bytes(M, N, K))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib.wq_linear_sparse_kernel(_p(x), M, K, _p(packed), _p(scales), _p(zeros), N, group,
                                      _p(row_ptr), _p(col) if nnz else None, _p(val) if nnz else None, nnz,
-                                     _p(out), y_dtype, KERNELS[kernel], None, 0, _stream(x))
+                                     _p(out), y_dtype, KERNELS[kernel], _p(workspace), wbytes, _stream(x))
     _check("wq_linear_sparse_kernel", rc)
     return out
 
 
-def linear(x, packed, scales, zeros, out_dtype=None, kernel: str = "auto", out=None, group: int = GROUP):
-    return linear_sparse(x, packed, scales, zeros, None, None, None, out_dtype, kernel, out, group)
+def linear(x, packed, scales, zeros, out_dtype=None, kernel: str = "auto", out=None, group: int = GROUP,
+           workspace=None):
+    return linear_sparse(x, packed, scales, zeros, None, None, None, out_dtype, kernel, out, group, workspace)
 
 
 def auto_kernel(M, N, K) -> str:

@@ -97,10 +97,9 @@ int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* 
 }
 
 size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) return 0;
+  if (N >= kMax32 / K || M >= kMax32 / K || M >= kMax32 / N) return 0;
+  return wq::gemm_workspace_bytes(M, N, K);
 }
 
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K) {
@@ -114,8 +113,6 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K, const uint3
                             const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
                             void* y, int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
                                    kernel);
   if (rc != WQ_OK) return rc;
@@ -126,7 +123,9 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K, const uint3
   if (kernel == WQ_KERNEL_GEMV)
     e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, as_stream(stream));
   else
-    e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, as_stream(stream));
+    e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32,
+                        workspace != nullptr && aligned(workspace, 16) ? workspace : nullptr, workspace_bytes,
+                        as_stream(stream));
   return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
 }
 

@@ -66,7 +66,11 @@ def test_workspace_sizes(lib):
     b = lib.wq_quantize_workspace_bytes(4096, 4096, 75497)
     assert b >= 4096 * 4096 // 8 + 3 * 4096 * 4 + 2048 * 4
     assert lib.wq_quantize_workspace_bytes(64, 100, 5) == 0      # invalid K
-    assert lib.wq_linear_workspace_bytes(512, 8192, 28672) == 0
+    # the prefill GEMM splits K only when its tile grid cannot fill the GPU
+    assert lib.wq_linear_workspace_bytes(2048, 14336, 4096) == 0
+    ws = lib.wq_linear_workspace_bytes(512, 8192, 28672)
+    assert ws > 0 and ws % (512 * 8192 * 4) == 0
+    assert lib.wq_linear_workspace_bytes(0, 8192, 28672) == 0
 
 
 def linear(lib, x=A, M=1, K=256, packed=A2, scales=A3, zeros=A4, N=64, group=128, row_ptr=None, col=None,
