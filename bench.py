@@ -152,6 +152,37 @@ def measure_offline(wq, torch, index):
     return dict(config=index, N=N, K=K, sparse_k=sk, ms=ms, weights_per_s=N * K / (ms * 1e-3))
 
 
+def kernel_source_hash():
+    """Short hash of the decode kernel source: a recorded traffic figure only
+    describes the kernel it was measured on."""
+    import hashlib
+    path = os.path.join(ROOT, "quantized_gemm_rtn_amd", "csrc", "gemv.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the decode kernel on the headline workload, from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a
+    device copy of known size), or None when that summary describes another
+    version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "gemv_decode_7b_up_proj_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle's linear (fp64 dequantize + BLAS matmul) on the headline
     workload, on this host's cores, repeated until the time budget is spent."""
@@ -187,6 +218,8 @@ def main():
     ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel],... "
                     "(default: the batched-decode, prefill and 70B-sweep set)")
     ap.add_argument("--no-offline", action="store_true", help="skip timing the offline quantizer")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run one device-to-device copy of BYTES first (reference for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer needs no collective and the build targets a single "
@@ -199,6 +232,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     wq.load()
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     head = measure(wq, torch, 2, 1, args.steps, args.warmup)
     print(f"# headline 2:1 {head['kernel']} {head['us_per_launch']:.2f} us  {head['GBps']:.1f} GB/s "
@@ -251,7 +291,7 @@ def main():
                    "M": 1, "N": 11008, "K": 4096, "group": 128, "kernel": head["kernel"],
                    "rotated_sets": head["rotated_sets"]},
         "roofline": {"bound": "hbm", "achieved": round(head["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["hbm_frac"], 4), "traffic": None},
+                     "frac": round(head["hbm_frac"], 4), "traffic": recorded_traffic()},
         "cpu_baseline": cpu,
         "workloads": rows,
         "offline": offline,
