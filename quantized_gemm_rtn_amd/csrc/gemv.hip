@@ -49,10 +49,16 @@ namespace wq {
 constexpr int kGemvWaves = 4;   // KW
 constexpr int kGemvDepth = 8;   // D: groups in flight per lane (128-bit weight loads)
 constexpr int kGemvDepthX = 4;  // D when each group also carries its activations
+constexpr int kGemvEarly = 8;   // weight groups issued before the wait on staged data
 constexpr int kXLdsMaxHalves = 32768;
-// sched_barrier mask: ALU, VALU, SALU, MFMA, LDS and transcendental instructions may
-// be scheduled across it, vector memory instructions may not.
-constexpr int kSchedAllButVmem = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x0400;
+// SZV value of gemv_lds_kernel for scales and zero-points held in registers (see below)
+constexpr int kSzInRegs = -1;
+// sched_barrier mask between consecutive groups of a window: scalar, MFMA, LDS and
+// transcendental instructions may be scheduled across it; vector memory and the
+// other vector ALU instructions may not. The weight refills then stay next to the
+// group that frees their register, and the unpacking of a word is not hoisted above
+// earlier groups (which would move the wait for its load up with it).
+constexpr int kSchedKeepGroups = 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x0400;
 
 // ---------------------------------------------------------------------------
 // Scale / zero-point staging: LDS sz[16][G + 1] = (s, 1024 + z) for the block's rows.
@@ -68,13 +74,14 @@ struct SzStage {
   uint16_t v1s[SZV == 1 ? C : 1], v1z[SZV == 1 ? C : 1];
 
   __device__ __forceinline__ void load(const f16* scales, const f16* zeros, int n0, int N, int G, int t) {
-    const int nload = SZV ? 16 * G / SZV : 0;
+    constexpr int V = SZV > 0 ? SZV : 1;
+    const int nload = 16 * G / V;
+    // the block's 16 rows are contiguous; past row N - 1 the last vector is repeated
+    const size_t o0 = (size_t)n0 * G, o_last = (size_t)N * G - V;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int idx = min(t + i * T, nload - 1);
-      const int e = idx * SZV;
-      const int row = e / G, c = e - row * G;
-      const size_t o = (size_t)min(n0 + row, N - 1) * G + c;
+      const size_t o = min(o0 + (size_t)idx * V, o_last);
       if constexpr (SZV == 8) {
         v8s[i] = *reinterpret_cast<const uint4*>(scales + o);
         v8z[i] = *reinterpret_cast<const uint4*>(zeros + o);
@@ -89,7 +96,7 @@ struct SzStage {
   __device__ __forceinline__ void store(f16x2* sz, const f16* scales, const f16* zeros, int n0, int N, int G,
                                         int t) {
     const f16 k1024 = (f16)1024.0f;
-    const int nload = SZV ? 16 * G / SZV : 0;
+    const int nload = 16 * G / (SZV > 0 ? SZV : 1);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int idx = min(t + i * T, nload - 1);
@@ -110,6 +117,65 @@ struct SzStage {
       }
     }
   }
+};
+
+// Sum over each 16-lane row of the wave (fixed order, a Hillis-Steele scan with
+// DPP row shifts that read 0 past the row start); the row total lands in its last
+// lane. DPP moves cost a VALU slot, where a lane shuffle through LDS would cost a
+// round trip per step.
+__device__ __forceinline__ float row16_sum_to_last(float v) {
+#define WQ_ROW_SHR(n) \
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + (n), 0xf, 0xf, true))
+  WQ_ROW_SHR(1);
+  WQ_ROW_SHR(2);
+  WQ_ROW_SHR(4);
+  WQ_ROW_SHR(8);
+#undef WQ_ROW_SHR
+  return v;
+}
+
+// Keeps the four registers of an MFMA result reserved until the group's epilogue
+// has consumed it (acc depends on it), in accumulation registers. With fewer than
+// four output rows stored, part[1..3] are never read; in blocks of more than 256
+// threads the compiler then put the MFMA result in ordinary vector registers and
+// handed the unread ones to other instructions while the MFMA could still be
+// writing them, which corrupted an LDS address (wrong results, no fault). An
+// accumulation-register operand here keeps them reserved and puts the MFMA in its
+// accumulation-register form, as in 256-thread blocks. No instruction is emitted.
+__device__ __forceinline__ void hold_accumulator(const f32x4& part, const f32x4& acc) {
+  asm volatile("" ::"a"(part), "v"(acc));
+}
+
+// (s, z) of a window of D groups in one load: 16 bytes for D = 8, 8 bytes for D = 4.
+template <int D> struct SzVecOf;
+template <> struct SzVecOf<8> { using type = uint4; };
+template <> struct SzVecOf<4> { using type = uint2; };
+template <int D> struct HalfWords { uint32_t w[D / 2]; };
+
+// Half i of a vector of fp16 values; i is a compile-time constant after unrolling.
+template <typename V>
+__device__ __forceinline__ f16 half_of(const V& v, int i) {
+  const auto a = __builtin_bit_cast(HalfWords<sizeof(V) / 2>, v);
+  const uint32_t w = a.w[i >> 1];
+  return bits_to_f16((uint16_t)((i & 1) ? w >> 16 : w & 0xffffu));
+}
+
+// A wave's ng groups are consumed in windows of D prefetched groups. Windows start
+// at 0, D, 2D, ...; when D does not divide ng, the last window is moved back to end
+// at group ng (so every load stays inside the wave's range and is prefetched like
+// the others) and its first D - ng % D groups, already done, are skipped. With
+// ng < D there is one window whose loads past ng repeat group ng - 1.
+struct Windows {
+  int n, nfull, last_lo, last_hi, ng, D;
+  __device__ Windows(int ng_, int D_) : ng(ng_), D(D_) {
+    nfull = ng / D;
+    const int rem = ng - nfull * D;
+    n = ng >= D ? nfull + (rem > 0) : (ng > 0);
+    last_lo = ng >= D && rem > 0 ? D - rem : 0;
+    last_hi = ng >= D ? D : ng;
+  }
+  // start of window b + 1, given the start gs of window b
+  __device__ int next(int b, int gs) const { return b + 1 < nfull ? gs + D : ng - D; }
 };
 
 // Fixed-order sum of the KW partial tiles through LDS and the single store.
@@ -149,19 +215,22 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   constexpr int T = 64 * KW;
   extern __shared__ __align__(16) char smem[];
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, in a scalar register
   const int r = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
   const int G = K >> 7;
   const int mrows = min(16, M - m0);
   const int SR = MR == 1 ? 1 : 4 * ((mrows + 3) >> 2);  // rows of the x-sum tables
-  // LDS: sz[16][G + 1] (s, 1024 + z) | xs[mrows][K] permuted, odd channels / 16 |
+  // LDS: sz[16][G + 1] (s, 1024 + z), unless SZV == kSzInRegs |
+  //      xs[mrows][K] permuted, odd channels / 16 |
   //      sums of x over even / odd channels per (group, row)
+  const size_t sz_bytes = SZV == kSzInRegs ? 0 : (size_t)16 * (G + 1) * 4;
   f16x2* sz = reinterpret_cast<f16x2*>(smem);
-  f16* xs = reinterpret_cast<f16*>(smem + (size_t)16 * (G + 1) * 4);
+  f16* xs = reinterpret_cast<f16*>(smem + sz_bytes);
   // x sums per group: [g][2][SR] (even rows then odd rows); with MR == 1, SR == 1
   // and the pair (even, odd) of row 0 is adjacent
-  float* sab = reinterpret_cast<float*>(smem + (size_t)16 * (G + 1) * 4 + (size_t)mrows * K * 2);
+  float* sab = reinterpret_cast<float*>(smem + sz_bytes + (size_t)mrows * K * 2);
 
   const int n_ld = min(n0 + r, N - 1);  // ragged N: load a valid row, never store it
   const uint32_t* wrow = packed + (size_t)n_ld * (size_t)(K >> 3) + 4 * h;
@@ -169,26 +238,39 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   const int ng = g_hi - g_lo;
 
   // ---- prologue: staging loads, weight prefetch, staging stores
-  SzStage<SZV, T> szs;
-  szs.load(scales, zeros, n0, N, G, t);
+  SzStage<SZV == kSzInRegs ? 8 : SZV, T> szs;
+  if constexpr (SZV != kSzInRegs) szs.load(scales, zeros, n0, N, G, t);
+  // the block's rows of x are contiguous in memory and in LDS
   const int x_vecs = mrows * (K >> 3);
+  const f16* xblk = x + (size_t)m0 * K;
   uint4 xv[XC];
 #pragma unroll
-  for (int i = 0; i < XC; ++i) {
-    const int idx = min(t + i * T, x_vecs - 1);
-    const int row = idx / (K >> 3), c8 = idx - row * (K >> 3);
-    xv[i] = *reinterpret_cast<const uint4*>(x + (size_t)(m0 + row) * K + 8 * c8);
-  }
-  const int nfull = ng / D;
-  const int g_first_valid = min(g_lo, G - 1);  // waves without groups still load valid memory
+  for (int i = 0; i < XC; ++i) xv[i] = *reinterpret_cast<const uint4*>(xblk + 8 * min(t + i * T, x_vecs - 1));
+  // in-register mode: each lane loads the (s, z) of its row for a window of D groups
+  // as two D-half vectors, issued with the window's weights
+  using SzVec = typename SzVecOf<D>::type;
+  const f16* s_row = scales + (size_t)n_ld * G + g_lo;
+  const f16* z_row = zeros + (size_t)n_ld * G + g_lo;
+  SzVec sv = {}, zv = {};
   uint4 wbuf[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    const int g = max(min(g_lo + i, g_hi - 1), g_first_valid);
+  auto prefetch = [&](int i) {
+    const int g = g_lo + min(i, max(ng - 1, 0));
     wbuf[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 16);
+  };
+  // The staging loads stay ahead of the weight loads (waits count loads in issue
+  // order). The first D0 weight groups go out before the wait on the staging loads,
+  // the others after it.
+  constexpr int D0 = kGemvEarly < D ? kGemvEarly : D;
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (SZV == kSzInRegs) {
+    sv = *reinterpret_cast<const SzVec*>(s_row);
+    zv = *reinterpret_cast<const SzVec*>(z_row);
   }
+#pragma unroll
+  for (int i = 0; i < D0; ++i) prefetch(i);
+  __builtin_amdgcn_sched_barrier(0);
 
-  szs.store(sz, scales, zeros, n0, N, G, t);
+  if constexpr (SZV != kSzInRegs) szs.store(sz, scales, zeros, n0, N, G, t);
   const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
   const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 #pragma unroll
@@ -204,24 +286,27 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
     uint4 q = p;
     q.y = as_u32(as_f16x2(p.y) * sixteenth);
     q.w = as_u32(as_f16x2(p.w) * sixteenth);
+    // unconditional (clamped lanes rewrite the values of the last vector), so the
+    // compiler cannot sink a staging load behind the weight prefetch
     *reinterpret_cast<uint4*>(xs + 8 * idx) = q;
-    // the 16 chunks of a group sit in 16 consecutive lanes: fixed-order butterfly
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      se += __shfl_xor(se, o, 16);
-      so += __shfl_xor(so, o, 16);
-    }
-    if ((idx_raw & 15) == 0 && idx_raw < x_vecs) {
-      const int row = idx_raw / (K >> 3), g = (idx_raw - row * (K >> 3)) >> 4;
-      if constexpr (MR == 1) {
+    // the 16 chunks of a group sit in one 16-lane row; its total lands in lane 15
+    se = row16_sum_to_last(se);
+    so = row16_sum_to_last(so);
+    if ((idx_raw & 15) == 15 && idx_raw < x_vecs) {
+      if constexpr (MR == 1) {  // a single row
+        const int g = idx_raw >> 4;
         sab[2 * g] = se;
         sab[2 * g + 1] = so;
       } else {
+        const int row = idx_raw / (K >> 3), g = (idx_raw - row * (K >> 3)) >> 4;
         sab[2 * g * SR + row] = se;
         sab[2 * g * SR + SR + row] = so;
       }
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = D0; i < D; ++i) prefetch(i);
   __syncthreads();
 
   // ---- main loop over this wave's groups
@@ -232,18 +317,28 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   const uint32_t magic = magic_1024x2();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto group = [&](const uint4& w, int g) {
+  // group g of the wave, the i-th of its window (i selects the in-register (s, z))
+  auto group = [&](const uint4& w, int g, int i) {
     const uint32_t wds[4] = {w.x, w.y, w.z, w.w};
+    // the four LDS reads go out together, so their latency is paid once per group
+    uint4 xa[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) xa[tt] = *reinterpret_cast<const uint4*>(xl + (size_t)g * 128 + 8 * tt);
+    __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // DS reads first
     f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const uint4 xa = *reinterpret_cast<const uint4*>(xl + (size_t)g * 128 + 8 * tt);
-      part = mfma_16x16x32(as_f16x8(xa), as_f16x8(codes_biased_x16(wds[tt], magic)), part);
+    for (int tt = 0; tt < 4; ++tt)
+      part = mfma_16x16x32(as_f16x8(xa[tt]), as_f16x8(codes_biased_x16(wds[tt], magic)), part);
+    float s, c1;  // c1 = 1024 + z
+    if constexpr (SZV == kSzInRegs) {
+      s = (float)half_of(sv, i);
+      c1 = (float)half_of(zv, i) + 1024.0f;
+    } else {
+      const f16x2 sbz = szr[g];
+      s = (float)sbz[0];
+      c1 = (float)sbz[1];
     }
-    const f16x2 sbz = szr[g];
-    const float s = (float)sbz[0];
-    const float c1 = (float)sbz[1];  // 1024 + z
-    const float c2 = c1 - 960.0f;     // 64 + z
+    const float c2 = c1 - 960.0f;  // 64 + z
     // only the first MR rows of a lane's four can be stored (MR < 4 when M <= 2)
     if constexpr (MR == 1) {
       const float2 eo = *reinterpret_cast<const float2*>(sab + 2 * g * SR);
@@ -254,32 +349,50 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
 #pragma unroll
       for (int i = 0; i < MR; ++i) acc[i] += s * (part[i] - c1 * e[i] - c2 * o[i]);
     }
+    hold_accumulator(part, acc);
   };
 
-  // blocks of D groups: each step consumes one buffered word, then refills the same
-  // register with the same step of the next block (consume first, so the refill can
-  // reuse the register and the loop carries no copy of an in-flight load)
-  int gb = 0;
-  const uint32_t* wnext = wrow + (size_t)(g_lo + D) * 16;
-  for (int b = 0; b + 1 < nfull; ++b, gb += D, wnext += D * 16) {
+  // windows of D groups: each step consumes one buffered word, then refills the same
+  // register with the same step of the next window (consume first, so the refill can
+  // reuse the register and the loop carries no copy of an in-flight load).
+  // In-register mode: the next window's (s, z) are loaded right after its first
+  // weight word, so they arrive before that word is consumed; the current window's
+  // are kept until its last group.
+  const Windows win(ng, D);
+  int gs = 0;
+  for (int b = 0; b + 1 < win.n; ++b) {
+    const int gs_next = win.next(b, gs);
+    const uint32_t* wn = wrow + (size_t)(g_lo + gs_next) * 16;
+    SzVec sn = sv, zn = zv;
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      group(wbuf[i], g_lo + gb + i);
-      wbuf[i] = *reinterpret_cast<const uint4*>(wnext + i * 16);
+      group(wbuf[i], g_lo + gs + i, i);
+      wbuf[i] = *reinterpret_cast<const uint4*>(wn + i * 16);
+      if constexpr (SZV == kSzInRegs) {
+        if (i == 0) {
+          sn = *reinterpret_cast<const SzVec*>(s_row + gs_next);
+          zn = *reinterpret_cast<const SzVec*>(z_row + gs_next);
+        }
+      }
       // keep the refill here: left alone, the scheduler sinks all refills to the end
-      // of the block, and the wave then waits for every load before issuing more.
-      // Only memory instructions are pinned; arithmetic may still overlap groups.
-      __builtin_amdgcn_sched_barrier(kSchedAllButVmem);
+      // of the window, and the wave then waits for every load before issuing more.
+      __builtin_amdgcn_sched_barrier(kSchedKeepGroups);
     }
+    sv = sn;
+    zv = zn;
+    gs = gs_next;
   }
-  if (nfull > 0) {
+  if (win.last_lo == 0 && win.last_hi == D) {  // a full last window, without branches
 #pragma unroll
-    for (int i = 0; i < D; ++i) group(wbuf[i], g_lo + gb + i);
-    gb += D;
+    for (int i = 0; i < D; ++i) group(wbuf[i], g_lo + gs + i, i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i >= win.last_lo && i < win.last_hi) group(wbuf[i], g_lo + gs + i, i);
   }
-  for (; gb < ng; ++gb) group(*reinterpret_cast<const uint4*>(wrow + (size_t)(g_lo + gb) * 16), g_lo + gb);
 
-  // ---- sparse outlier term for column n = n0 + r, activations from LDS
+  // ---- sparse outlier term for column n = n0 + r (entries split over the KW
+  // waves), activations from LDS
   const int n = n0 + r;
   if (row_ptr != nullptr && n < N) {
     const int e1 = row_ptr[n + 1];
@@ -308,7 +421,8 @@ gemv_stream_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __re
   constexpr int T = 64 * KW;
   extern __shared__ __align__(16) char smem[];
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, in a scalar register
   const int r = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
   const int G = K >> 7;
@@ -325,7 +439,6 @@ gemv_stream_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __re
   SzStage<SZV, T> szs;
   szs.load(scales, zeros, n0, N, G, t);
   // each group's activations travel with its weights (same prefetch unit, same order)
-  const int nfull = ng / D;
   const int g_first_valid = min(g_lo, G - 1);
   uint4 wbuf[D];
   uint4 xbuf[D][4];
@@ -350,34 +463,28 @@ gemv_stream_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __re
     for (int tt = 0; tt < 4; ++tt)
       part = mfma_16x16x32(as_f16x8(perm_x8(xg[tt])), codes_minus_zero(wds[tt], bias), part);
     acc += (float)sbz[0] * part;
+    hold_accumulator(part, acc);
   };
 
-  int gb = 0;
-  for (int b = 0; b + 1 < nfull; ++b, gb += D) {
+  const Windows win(ng, D);
+  int gs = 0;
+  for (int b = 0; b + 1 < win.n; ++b) {
+    const int gs_next = win.next(b, gs);
+    const uint32_t* wn = wrow + (size_t)(g_lo + gs_next) * 16;
+    const f16* xn = xrow + (size_t)(g_lo + gs_next) * 128;
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      const int g = g_lo + gb + i;
-      group(wbuf[i], xbuf[i], g);
-      wbuf[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)(g + D) * 16);
+      group(wbuf[i], xbuf[i], g_lo + gs + i);
+      wbuf[i] = *reinterpret_cast<const uint4*>(wn + i * 16);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        xbuf[i][tt] = *reinterpret_cast<const uint4*>(xrow + (size_t)(g + D) * 128 + 8 * tt);
-      __builtin_amdgcn_sched_barrier(kSchedAllButVmem);  // keep the refill next to its consumption
+      for (int tt = 0; tt < 4; ++tt) xbuf[i][tt] = *reinterpret_cast<const uint4*>(xn + i * 128 + 8 * tt);
+      __builtin_amdgcn_sched_barrier(kSchedKeepGroups);  // keep the refill next to its consumption
     }
+    gs = gs_next;
   }
-  if (nfull > 0) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) group(wbuf[i], xbuf[i], g_lo + gb + i);
-    gb += D;
-  }
-  for (; gb < ng; ++gb) {
-    const int g = g_lo + gb;
-    const uint4 w = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 16);
-    uint4 xg[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) xg[tt] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 128 + 8 * tt);
-    group(w, xg, g);
-  }
+  for (int i = 0; i < D; ++i)
+    if (i >= win.last_lo && i < win.last_hi) group(wbuf[i], xbuf[i], g_lo + gs + i);
 
   const int n = n0 + r;
   if (row_ptr != nullptr && n < N) {
@@ -428,7 +535,8 @@ static hipError_t launch_lds(const uint16_t* x, int64_t M, int64_t K, const uint
                              const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
   static size_t lds_set = 0;
   const int64_t G = K / kGroup, mrows = M < 16 ? M : 16, SR = MR == 1 ? 1 : 4 * ((mrows + 3) / 4);
-  const size_t lds = (size_t)16 * (G + 1) * 4 + (size_t)mrows * K * 2 + (size_t)2 * G * SR * 4;
+  const size_t lds = (SZV == kSzInRegs ? 0 : (size_t)16 * (G + 1) * 4) + (size_t)mrows * K * 2 +
+                     (size_t)2 * G * SR * 4;
   return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR>, lds, x, M, K, packed, scales, zeros, N,
                      row_ptr, col, val, y, y_f32, stream, &lds_set);
 }
@@ -448,23 +556,31 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
                        const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
   const int64_t G = K / kGroup;
   const int64_t mrows_max = M < 16 ? M : 16;
-  // activations fit in LDS next to the scales: stage them once per block, with the
-  // fewest staging registers that cover them
-  const int64_t xloads = (mrows_max * K / 8 + 64 * kGemvWaves - 1) / (64 * kGemvWaves);
-  const int xc = mrows_max * K > kXLdsMaxHalves ? 0 : xloads <= 2 ? 2 : xloads <= 4 ? 4 : xloads <= 8 ? 8 : 16;
   // scales/zeros rows as 16-byte vectors when every row starts 16-byte aligned
   const bool vec = G % 8 == 0 && G <= 256 && reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(zeros) % 16 == 0;
   const int sv = vec ? 8 : (G <= 256 ? 1 : 0);
-#define WQ_ARGS x, M, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, stream
+  // scales and zero-points in registers, two loads per window of D groups: every
+  // wave's window starts on a multiple of D groups
+  static_assert(kGemvDepth == 4 || kGemvDepth == 8, "in-register (s, z) windows hold 4 or 8 groups");
+  const bool in_regs = vec && G % (kGemvDepth * kGemvWaves) == 0;
+  const int sz_mode = in_regs ? kSzInRegs : sv;
   // output rows a lane can hold: rows 4h .. 4h+3 of the tile, so M = 1, 2 need fewer
   const int mr = mrows_max == 1 ? 1 : (mrows_max == 2 ? 2 : 4);
+  // activations fit in LDS next to the scales: stage them once per block, with the
+  // fewest staging registers that cover them
+  const int64_t xloads = (mrows_max * K / 8 + 64 * kGemvWaves - 1) / (64 * kGemvWaves);
+  const int xc = mrows_max * K > kXLdsMaxHalves ? 0
+                 : xloads <= 1 ? 1 : xloads <= 2 ? 2 : xloads <= 4 ? 4 : xloads <= 8 ? 8 : 16;
+#define WQ_ARGS x, M, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, stream
 #define WQ_LDS(XC, SV, MR) \
-  if (xc == XC && sv == SV && mr == MR) return launch_lds<XC, SV, MR>(WQ_ARGS)
+  if (xc == XC && sz_mode == SV && mr == MR) return launch_lds<XC, SV, MR>(WQ_ARGS)
 #define WQ_LDS_MR(XC, SV) WQ_LDS(XC, SV, 1); WQ_LDS(XC, SV, 2); WQ_LDS(XC, SV, 4)
-  WQ_LDS_MR(2, 8); WQ_LDS_MR(4, 8); WQ_LDS_MR(8, 8); WQ_LDS_MR(16, 8);
-  WQ_LDS_MR(2, 1); WQ_LDS_MR(4, 1); WQ_LDS_MR(8, 1); WQ_LDS_MR(16, 1);
-  WQ_LDS_MR(2, 0); WQ_LDS_MR(4, 0); WQ_LDS_MR(8, 0); WQ_LDS_MR(16, 0);
+  WQ_LDS_MR(1, kSzInRegs); WQ_LDS_MR(2, kSzInRegs); WQ_LDS_MR(4, kSzInRegs); WQ_LDS_MR(8, kSzInRegs);
+  WQ_LDS_MR(16, kSzInRegs);
+  WQ_LDS_MR(1, 8); WQ_LDS_MR(2, 8); WQ_LDS_MR(4, 8); WQ_LDS_MR(8, 8); WQ_LDS_MR(16, 8);
+  WQ_LDS_MR(1, 1); WQ_LDS_MR(2, 1); WQ_LDS_MR(4, 1); WQ_LDS_MR(8, 1); WQ_LDS_MR(16, 1);
+  WQ_LDS_MR(1, 0); WQ_LDS_MR(2, 0); WQ_LDS_MR(4, 0); WQ_LDS_MR(8, 0); WQ_LDS_MR(16, 0);
 #undef WQ_LDS_MR
   if (sv == 8) return launch_stream<8>(WQ_ARGS);
   if (sv == 1) return launch_stream<1>(WQ_ARGS);
