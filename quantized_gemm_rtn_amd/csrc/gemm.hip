@@ -201,6 +201,7 @@ gemm_kernel(GemmArgs a) {
     }
   }
 
+  const uint32_t magic = magic_1024x2();
   const int nk = (ke - kb) / kBK;
   if (nk > 0) {
     load_step(kb);
@@ -229,11 +230,11 @@ gemm_kernel(GemmArgs a) {
                                                 8 * (4 * h + ks));
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const f16 zb = (f16)1024.0f + zc[j];
-        const f16x2 bias = {zb, zb};
+        const f16 zb = (f16)1024.0f + zc[j], zn = -((f16)64.0f + zc[j]);
+        const f16x2 bias = {zb, zb}, nbias16 = {zn, zn};
         const f16x2 s2 = {sc[j], sc[j]};
         const uint32_t w = ks == 0 ? wc[j].x : ks == 1 ? wc[j].y : ks == 2 ? wc[j].z : wc[j].w;
-        uint4 d = dequant_word(w, bias, s2);
+        uint4 d = dequant_word_x16(w, magic, bias, nbias16, s2);
         // sparse entries of this column inside this lane's eight input channels
         // [kc, kc + 8) are added to the dequantized weight (entries below kc belong
         // to the other half-wave's channels and are skipped)
@@ -302,6 +303,448 @@ gemm_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dense kernel for large M. One block of four waves per compute unit, block tile
+// 256 x 256, wave tile 128 x 128 (4 x 4 subtiles of 32 x 32, accumulators in the
+// accumulation registers). K is consumed in super-steps of one quantization group
+// (128), each split into eight MFMA sub-steps of 16.
+//  - Weights, scales and zero-points of super-step s + 1 are loaded at the start of
+//    super-step s into the other of two register sets, a whole super-step (128
+//    MFMAs per wave) ahead of their use; activations of s + 1 are loaded at the same
+//    time and written to the other of two LDS stages at the end of s.
+//  - Within a super-step the A fragments and dequantized B operands of sub-step
+//    ks + 1 are prepared while the 16 MFMAs of sub-step ks run.
+//  - Lane l = 32h + c of a wave supplies column c of each 32-wide subtile; in
+//    sub-step ks it feeds the eight input channels 64 (ks / 4) + 32h + 8 (ks % 4)
+//    of the group: word 8 (ks / 4) + 4h + ks % 4 of the column's 16 words, so its
+//    weights for the group are two 16-byte loads.
+constexpr int kBigSS = 128;                // halves per super-step (one group)
+constexpr int kBigStride = kBigSS + 8;     // halves per LDS row: 68 dwords, 4 mod 32
+constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 groups x 256 columns
+
+template <int BM, int BN, int WGM, int WGN, int MINB>
+__global__ void __launch_bounds__(256, MINB)
+gemm_big_kernel(GemmArgs a) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MT = WTM / 32, NT = WTN / 32;
+  constexpr int XV = BM * (kBigSS / 8) / 256;  // 16-byte activation loads per thread per super-step
+  constexpr int XP = XV / 4;                    // ... per part
+  constexpr int STAGE = BM * kBigStride;
+  static_assert(WGM * WGN == 4 && BN == 256 && XP * 4 == XV && NT <= 4 && MT >= 1, "tile/thread mismatch");
+
+  extern __shared__ __align__(16) f16 smem[];
+  // LDS: two activation stages | (s, z) table szl[buffer][group of the pair][column]
+  uint32_t* szl = reinterpret_cast<uint32_t*>(smem + 2 * STAGE);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int h = lane >> 5, c32 = lane & 31;
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K >> 7;  // even (the launcher sends odd G to the other kernel)
+
+  const int ntile = a.tiles_m * a.tiles_n;
+  const int nblk = ntile * a.ksplit;
+  int bid = blockIdx.x;
+  if (nblk % kNumXcd == 0) bid = (bid % kNumXcd) * (nblk / kNumXcd) + bid / kNumXcd;
+  const int slice = bid / ntile;
+  const int tile = bid - slice * ntile;
+  const int m0 = (tile % a.tiles_m) * BM, n0 = (tile / a.tiles_m) * BN;
+  const int g0 = slice * (a.k_per_slice >> 7);                  // even
+  const int ng = min(G, g0 + (a.k_per_slice >> 7)) - g0;        // even
+
+  // Offsets are unsigned 32-bit element offsets from the (scalar) base pointers, so
+  // loads take the scalar-base form without 64-bit address arithmetic (M*K and N*K
+  // are below 2^31).
+  // activation producer: thread t loads rows (t >> 4) + 16 i, 16-byte chunk t & 15
+  // (rows beyond M reread row M - 1)
+  const int xch = t & 15, xrow0 = m0 + (t >> 4);
+  const int xdst0 = (t >> 4) * kBigStride + 8 * xch;
+  // weight columns of this lane
+  uint32_t woff[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const uint32_t n = (uint32_t)min(n0 + wn * WTN + 32 * j + c32, N - 1);
+    woff[j] = n * (uint32_t)(K >> 3) + 4 * h;
+  }
+  // (s, z) producer: thread t stages column n0 + t for the two groups of a pair
+  const uint32_t szoff = (uint32_t)min(n0 + t, N - 1) * (uint32_t)G + (uint32_t)g0;
+
+  struct WSet {
+    uint4 w[NT][2];
+  };
+  WSet wa, wb;
+  uint4 xr[XV];
+  uint32_t sp = 0, zp = 0;  // staged (s, z) of a pair: fp16 pairs (group 2q, 2q + 1)
+  // the loads of super-step g in four parts (part p: activation loads XP p ..
+  // XP (p + 1) - 1 and the weights of column subtile p), issued over the first four
+  // sub-steps; the activation stores in four parts over the last four (clamped past
+  // the slice)
+  auto load_part = [&](WSet& W, int g, int p) {
+    const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
+    const uint32_t k0 = 128 * gg + 8 * xch;
+#pragma unroll
+    for (int i = XP * p; i < XP * p + XP; ++i) {
+      const uint32_t row = (uint32_t)min(xrow0 + 16 * i, M - 1);
+      xr[i] = *reinterpret_cast<const uint4*>(a.x + (row * (uint32_t)K + k0));
+    }
+    if (p < NT) {
+      const uint32_t o = woff[p] + 16 * gg;
+      W.w[p][0] = *reinterpret_cast<const uint4*>(a.packed + o);
+      W.w[p][1] = *reinterpret_cast<const uint4*>(a.packed + o + 8);
+    }
+  };
+  auto store_part = [&](f16* st, int p) {
+#pragma unroll
+    for (int i = XP * p; i < XP * p + XP; ++i)
+      *reinterpret_cast<uint4*>(st + xdst0 + 16 * i * kBigStride) = perm_x8(xr[i]);
+  };
+  // (s, z) of the pair starting at super-step g (g even, clamped past the slice)
+  auto load_sz = [&](int g) {
+    const uint32_t o = szoff + (uint32_t)min(g, ng - 2);
+    sp = *reinterpret_cast<const uint32_t*>(a.scales + o);
+    zp = *reinterpret_cast<const uint32_t*>(a.zeros + o);
+  };
+  auto store_sz = [&](int buf) {
+    szl[(2 * buf) * 256 + t] = (sp & 0xFFFFu) | (zp << 16);
+    szl[(2 * buf + 1) * 256 + t] = (sp >> 16) | (zp & 0xFFFF0000u);
+  };
+  auto read_sz = [&](uint32_t (&sz)[NT], int buf, int grp) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) sz[j] = szl[(2 * buf + grp) * 256 + wn * WTN + 32 * j + c32];
+  };
+  const uint32_t magic = magic_1024x2();
+  auto read_a = [&](f16x8 (&av)[MT], const f16* xs, int ks) {
+    const int kk = 64 * (ks >> 2) + 32 * h + 8 * (ks & 3);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      av[i] = *reinterpret_cast<const f16x8*>(xs + (wm * WTM + 32 * i + c32) * kBigStride + kk);
+  };
+  auto deq_b = [&](const WSet& W, int j, int ks, uint32_t sz) {
+    const f16x2 sz2 = as_f16x2(sz);  // (s, z)
+    const f16 zb = (f16)1024.0f + sz2[1], zn = -((f16)64.0f + sz2[1]);
+    const f16x2 bias = {zb, zb}, nbias16 = {zn, zn}, s2 = {sz2[0], sz2[0]};
+    const uint4& q = W.w[j][ks >> 2];
+    const int c = ks & 3;
+    const uint32_t w = c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+    return as_f16x8(dequant_word_x16(w, magic, bias, nbias16, s2));
+  };
+
+  f32x16 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // One super-step (position pp in its pair, (s, z) table buffer buf): W holds its
+  // weights, Wn receives those of the next one; activations are read from stage xs
+  // and the next ones written to stage xn (last read before the barrier that ended
+  // the previous super-step). The A fragments of sub-step ks + 1 are read during
+  // sub-step ks, and the B operand of the next column (of the next sub-step, or of
+  // the next super-step after the last column) is unpacked during the four MFMAs of
+  // the current one: a wave issues in order, so vector work placed between its MFMAs
+  // runs while the matrix core is busy instead of beside it. The (s, z) of pair q + 1
+  // are loaded in the second super-step of pair q - 1 and staged in the first of
+  // pair q, a barrier before they are first read.
+  f16x8 a0[MT], a1[MT];
+  f16x8 bcur;
+  uint32_t szc[NT], szn[NT];
+  auto superstep = [&](const WSet& W, WSet& Wn, const f16* xs, f16* xn, int g, int pp, int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      f16x8 (&cur)[MT] = (ks & 1) ? a1 : a0;
+      f16x8 (&nxt)[MT] = (ks & 1) ? a0 : a1;
+      if (ks < 4) load_part(Wn, g + 1, ks);
+      if (ks >= 4) store_part(xn, ks - 4);
+      if (ks == 0 && pp == 1) load_sz(g + 3);
+      if (ks == 4 && pp == 0) store_sz(buf ^ 1);
+      if (ks == 6) read_sz(szn, pp == 0 ? buf : buf ^ 1, pp ^ 1);  // the next super-step's
+      if (ks < 7) read_a(nxt, xs, ks + 1);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const f16x8 bnext = j + 1 < NT ? deq_b(W, j + 1, ks, szc[j + 1])
+                                       : (ks < 7 ? deq_b(W, 0, ks + 1, szc[0]) : deq_b(Wn, 0, 0, szn[0]));
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i][j] = mfma_32x32x16(cur[i], bcur, acc[i][j]);
+        bcur = bnext;
+      }
+      // per column: MFMA, VALU, an LDS read (the A reads of the next sub-step), the
+      // column's share of the loads (sub-steps 0-3) or of the activation stores
+      // (4-7), then (MFMA, VALU) for the column's other row subtiles: about 16 VALU
+      // (the next operand's unpacking) spread over its MT MFMAs
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16 / MT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (ks < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+#pragma unroll
+        for (int r = 1; r < MT; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 16 / MT, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    read_a(a0, xn, 0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) szc[j] = szn[j];
+  };
+
+  if (ng > 0) {
+    // prologue: (s, z) of pairs 0 (staged) and 1 (in registers), activations and
+    // weights of super-step 0
+    load_sz(0);
+    store_sz(0);
+    load_sz(2);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) load_part(wa, 0, p);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) store_part(smem, p);
+    __syncthreads();
+    read_a(a0, smem, 0);
+    read_sz(szc, 0, 0);
+    bcur = deq_b(wa, 0, 0, szc[0]);
+    for (int g = 0; g < ng; g += 2) {
+      const int buf = (g >> 1) & 1;
+      superstep(wa, wb, smem, smem + STAGE, g, 0, buf);
+      superstep(wb, wa, smem + STAGE, smem, g + 1, 1, buf);
+    }
+  }
+
+  // store: the final y, or this slice's fp32 partial tile
+  const bool partial = a.ksplit > 1;
+  const uint32_t MN = (uint32_t)M * (uint32_t)N;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n0 + wn * WTN + 32 * j + c32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + wm * WTM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (m < M) {
+          const uint32_t o = (uint32_t)m * (uint32_t)N + (uint32_t)n;
+          if (partial)
+            static_cast<float*>(a.y)[(size_t)slice * MN + o] = acc[i][j][q];
+          else if (a.y_f32)
+            static_cast<float*>(a.y)[o] = acc[i][j][q];
+          else
+            static_cast<f16*>(a.y)[o] = (f16)acc[i][j][q];
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dense kernel for 16 < M <= 64: block tile 64 x 256, four waves of 64 x 64 (2 x 2
+// subtiles of 32 x 32), two blocks per compute unit, K split across blocks. At this M
+// the product streams the weights, and a super-step of one group is only 32 MFMAs per
+// wave, so the weights are loaded three super-steps ahead into a ring of four
+// register sets, and the activations two super-steps ahead (through two register
+// sets and two LDS stages). The loop body is four super-steps, so every ring index
+// is a constant (slices are multiples of four groups).
+template <int MINB>
+__global__ void __launch_bounds__(256, MINB)
+gemm_skinny_kernel(GemmArgs a) {
+  constexpr int BM = 64, BN = 256, WTN = 64, MT = 2, NT = 2;
+  constexpr int STAGE = BM * kBigStride;
+
+  extern __shared__ __align__(16) f16 smem[];
+  uint32_t* szl = reinterpret_cast<uint32_t*>(smem + 2 * STAGE);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h = lane >> 5, c32 = lane & 31;
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K >> 7;  // a multiple of 4
+
+  const int ntile = a.tiles_m * a.tiles_n;
+  const int nblk = ntile * a.ksplit;
+  int bid = blockIdx.x;
+  if (nblk % kNumXcd == 0) bid = (bid % kNumXcd) * (nblk / kNumXcd) + bid / kNumXcd;
+  const int slice = bid / ntile;
+  const int tile = bid - slice * ntile;
+  const int m0 = (tile % a.tiles_m) * BM, n0 = (tile / a.tiles_m) * BN;
+  const int g0 = slice * (a.k_per_slice >> 7);                  // a multiple of 4
+  const int ng = min(G, g0 + (a.k_per_slice >> 7)) - g0;        // a multiple of 4
+
+  // activations: thread t loads row (t >> 4) + 16 i (i < 4), 16-byte chunk t & 15
+  const int xch = t & 15, xrow0 = m0 + (t >> 4);
+  const int xdst0 = (t >> 4) * kBigStride + 8 * xch;
+  uint32_t woff[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const uint32_t n = (uint32_t)min(n0 + wn * WTN + 32 * j + c32, N - 1);
+    woff[j] = n * (uint32_t)(K >> 3) + 4 * h;
+  }
+  const uint32_t szoff = (uint32_t)min(n0 + t, N - 1) * (uint32_t)G + (uint32_t)g0;
+
+  uint4 w0[NT][2], w1[NT][2], w2[NT][2], w3[NT][2];  // weight ring
+  uint4 xa[4], xb[4];                                // activation register sets
+  uint32_t sp = 0, zp = 0;
+  auto wset = [&](int r) -> uint4(&)[NT][2] { return r == 0 ? w0 : r == 1 ? w1 : r == 2 ? w2 : w3; };
+  auto load_w_part = [&](uint4 (&W)[NT][2], int g, int j) {
+    const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
+    const uint32_t o = woff[j] + 16 * gg;
+    W[j][0] = *reinterpret_cast<const uint4*>(a.packed + o);
+    W[j][1] = *reinterpret_cast<const uint4*>(a.packed + o + 8);
+  };
+  auto load_x_part = [&](uint4 (&X)[4], int g, int i) {
+    const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
+    const uint32_t row = (uint32_t)min(xrow0 + 16 * i, M - 1);
+    X[i] = *reinterpret_cast<const uint4*>(a.x + (row * (uint32_t)K + 128 * gg + 8 * xch));
+  };
+  auto store_x_part = [&](const uint4 (&X)[4], f16* st, int i) {
+    *reinterpret_cast<uint4*>(st + xdst0 + 16 * i * kBigStride) = perm_x8(X[i]);
+  };
+  auto load_sz = [&](int g) {
+    const uint32_t o = szoff + (uint32_t)min(g, ng - 2);
+    sp = *reinterpret_cast<const uint32_t*>(a.scales + o);
+    zp = *reinterpret_cast<const uint32_t*>(a.zeros + o);
+  };
+  auto store_sz = [&](int buf) {
+    szl[(2 * buf) * 256 + t] = (sp & 0xFFFFu) | (zp << 16);
+    szl[(2 * buf + 1) * 256 + t] = (sp >> 16) | (zp & 0xFFFF0000u);
+  };
+  auto read_sz = [&](uint32_t (&sz)[NT], int buf, int grp) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) sz[j] = szl[(2 * buf + grp) * 256 + wn * WTN + 32 * j + c32];
+  };
+  const uint32_t magic = magic_1024x2();
+  auto read_a = [&](f16x8 (&av)[MT], const f16* xs, int ks) {
+    const int kk = 64 * (ks >> 2) + 32 * h + 8 * (ks & 3);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) av[i] = *reinterpret_cast<const f16x8*>(xs + (32 * i + c32) * kBigStride + kk);
+  };
+  auto deq_b = [&](const uint4 (&W)[NT][2], int j, int ks, uint32_t sz) {
+    const f16x2 sz2 = as_f16x2(sz);
+    const f16 zb = (f16)1024.0f + sz2[1], zn = -((f16)64.0f + sz2[1]);
+    const f16x2 bias = {zb, zb}, nbias16 = {zn, zn}, s2 = {sz2[0], sz2[0]};
+    const uint4& q = W[j][ks >> 2];
+    const int c = ks & 3;
+    const uint32_t w = c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+    return as_f16x8(dequant_word_x16(w, magic, bias, nbias16, s2));
+  };
+
+  f32x16 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  f16x8 a0[MT], a1[MT];
+  f16x8 bcur;
+  uint32_t szc[NT], szn[NT];
+  // super-step g = 4 it + i: weights of set i, activations from stage i % 2; loads the
+  // weights of g + 3 into set (i + 3) % 4 and the activations of g + 2 into register
+  // set i % 2, and stores those of g + 1 (register set (i + 1) % 2) to stage (i + 1) % 2
+  auto superstep = [&](int g, int i) {
+    const uint4(&W)[NT][2] = wset(i);
+    uint4(&Wl)[NT][2] = wset((i + 3) & 3);
+    uint4(&Xl)[4] = (i & 1) ? xb : xa;
+    const uint4(&Xs)[4] = (i & 1) ? xa : xb;
+    const f16* xs = smem + (i & 1) * STAGE;
+    f16* xn = smem + ((i + 1) & 1) * STAGE;
+    const int pp = i & 1, buf = (i >> 1) & 1;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      f16x8(&cur)[MT] = (ks & 1) ? a1 : a0;
+      f16x8(&nxt)[MT] = (ks & 1) ? a0 : a1;
+      if (ks < 4) load_x_part(Xl, g + 2, ks);
+      if (ks < NT) load_w_part(Wl, g + 3, ks);
+      if (ks >= 4) store_x_part(Xs, xn, ks - 4);
+      if (ks == 0 && pp == 1) load_sz(g + 3);
+      if (ks == 4 && pp == 0) store_sz(buf ^ 1);
+      if (ks == 6) read_sz(szn, pp == 0 ? buf : buf ^ 1, pp ^ 1);
+      if (ks < 7) read_a(nxt, xs, ks + 1);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const f16x8 bnext = j + 1 < NT ? deq_b(W, j + 1, ks, szc[j + 1])
+                                       : (ks < 7 ? deq_b(W, 0, ks + 1, szc[0])
+                                                 : deq_b(wset((i + 1) & 3), 0, 0, szn[0]));
+#pragma unroll
+        for (int r = 0; r < MT; ++r) acc[r][j] = mfma_32x32x16(cur[r], bcur, acc[r][j]);
+        bcur = bnext;
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (ks < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    read_a(a0, xn, 0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) szc[j] = szn[j];
+  };
+
+  if (ng > 0) {
+    load_sz(0);
+    store_sz(0);
+    load_sz(2);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      load_w_part(w0, 0, j);
+      load_w_part(w1, 1, j);
+      load_w_part(w2, 2, j);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      load_x_part(xa, 0, i);
+      load_x_part(xb, 1, i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_x_part(xa, smem, i);
+    __syncthreads();
+    read_a(a0, smem, 0);
+    read_sz(szc, 0, 0);
+    bcur = deq_b(w0, 0, 0, szc[0]);
+    for (int g = 0; g < ng; g += 4) {
+      superstep(g, 0);
+      superstep(g + 1, 1);
+      superstep(g + 2, 2);
+      superstep(g + 3, 3);
+    }
+  }
+
+  const bool partial = a.ksplit > 1;
+  const uint32_t MN = (uint32_t)M * (uint32_t)N;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n0 + wn * WTN + 32 * j + c32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (m < M) {
+          const uint32_t o = (uint32_t)m * (uint32_t)N + (uint32_t)n;
+          if (partial)
+            static_cast<float*>(a.y)[(size_t)slice * MN + o] = acc[i][j][q];
+          else if (a.y_f32)
+            static_cast<float*>(a.y)[o] = acc[i][j][q];
+          else
+            static_cast<f16*>(a.y)[o] = (f16)acc[i][j][q];
+        }
+      }
+    }
+}
+
 // y = sum over slices s = 0..S-1 of ws[s] (fixed order), in the output dtype.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ ws, int S, size_t MN, void* __restrict__ y, int y_f32) {
@@ -318,27 +761,69 @@ splitk_reduce_kernel(const float* __restrict__ ws, int S, size_t MN, void* __res
 
 struct GemmPlan {
   int bm, bn;
+  int kind;  // 0: gemm_kernel, 1: gemm_big_kernel 256 x 256, 2: gemm_big_kernel 64 x 256
   int ksplit, k_per_slice;
 };
 
 // Tile and split choice for M x N x K (shared by the launcher and the workspace query).
-static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+// Dense products take gemm_big_kernel above M = 128 (an even number of groups) and
+// gemm_skinny_kernel for M <= 64 (a multiple of four groups); the others (and every
+// product with a CSR term) take gemm_kernel.
+static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
   GemmPlan p;
-  p.bm = M <= 64 ? 64 : 128;
+  const int64_t G = K / 128;
+  p.kind = sparse ? 0 : (M > 128 && G % 2 == 0 ? 1 : (M <= 64 && G % 4 == 0 ? 2 : 0));
+  p.bm = p.kind == 1 ? 256 : (M <= 64 ? 64 : 128);
   p.bn = 256;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-  const int64_t ksteps = K / kBK;
   int64_t s = 1;
-  // split K while the grid is below two blocks per CU and each slice keeps >= 16 steps
-  while (tiles * s * 2 <= 512 && ksteps / (s * 2) >= 16) s *= 2;
-  p.ksplit = (int)s;
-  p.k_per_slice = (int)(((ksteps + s - 1) / s) * kBK);
+  if (p.kind != 0) {
+    // split K while the grid is below one (256 x 256) or two (64 x 256) blocks per CU
+    // and each slice keeps >= 8 groups; slices are an even number of groups
+    const int64_t target = p.kind == 1 ? 256 : 512;
+    const int64_t groups = K / 128;
+    while (tiles * s * 2 <= target && groups / (s * 2) >= 8) s *= 2;
+    p.ksplit = (int)s;
+    const int64_t q = p.kind == 1 ? 2 : 4;  // slices: a multiple of q groups
+    const int64_t per = ((groups + s - 1) / s + q - 1) / q * q;
+    p.k_per_slice = (int)(per * 128);
+  } else {
+    const int64_t ksteps = K / kBK;
+    // split K while the grid is below two blocks per CU and each slice keeps >= 16 steps
+    while (tiles * s * 2 <= 512 && ksteps / (s * 2) >= 16) s *= 2;
+    p.ksplit = (int)s;
+    p.k_per_slice = (int)(((ksteps + s - 1) / s) * kBK);
+  }
   return p;
 }
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const GemmPlan p = plan_gemm(M, N, K);
+static size_t plan_workspace(const GemmPlan& p, int64_t M, int64_t N) {
   return p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
+}
+
+// enough for the dense and the sparse plan of the shape
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const size_t a = plan_workspace(plan_gemm(M, N, K, false), M, N);
+  const size_t b = plan_workspace(plan_gemm(M, N, K, true), M, N);
+  return a > b ? a : b;
+}
+
+template <int BM, int BN, int WGM, int WGN, int MINB>
+static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
+  constexpr size_t lds = 2 * (size_t)BM * kBigStride * sizeof(f16) + kBigSzBytes;
+  auto kern = gemm_big_kernel<BM, BN, WGM, WGN, MINB>;
+  static bool attr_done = false;  // setting the same attribute twice is harmless
+  if (!attr_done) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  const int64_t nblk = (int64_t)a.tiles_m * a.tiles_n * a.ksplit;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), lds, stream, a);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int WGM, int WGN, bool SPARSE>
@@ -359,6 +844,16 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MINB>
+static hipError_t launch_skinny(GemmArgs a, hipStream_t stream) {
+  constexpr size_t lds = 2 * (size_t)64 * kBigStride * sizeof(f16) + kBigSzBytes;
+  a.tiles_m = (a.M + 63) / 64;
+  a.tiles_n = (a.N + 255) / 256;
+  const int64_t nblk = (int64_t)a.tiles_m * a.tiles_n * a.ksplit;
+  hipLaunchKernelGGL(gemm_skinny_kernel<MINB>, dim3((unsigned)nblk), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,
@@ -366,8 +861,9 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   constexpr int64_t kRowsPerLaunch = (int64_t)1 << 20;  // keeps the block count within int range
   for (int64_t m = 0; m < M; m += kRowsPerLaunch) {
     const int64_t mc = M - m < kRowsPerLaunch ? M - m : kRowsPerLaunch;
-    GemmPlan p = plan_gemm(mc, N, K);
-    const size_t need = p.ksplit > 1 ? (size_t)p.ksplit * mc * N * 4 : 0;
+    const bool sp = row_ptr != nullptr;
+    GemmPlan p = plan_gemm(mc, N, K, sp);
+    const size_t need = plan_workspace(p, mc, N);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
       p.ksplit = 1;  // no (or too small) workspace: run unsplit
       p.k_per_slice = (int)K;
@@ -391,8 +887,11 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.ksplit = p.ksplit;
     a.k_per_slice = p.k_per_slice;
     hipError_t e;
-    const bool sp = row_ptr != nullptr;
-    if (p.bm == 64)
+    if (p.kind == 1)
+      e = launch_big<256, 256, 2, 2, 1>(a, stream);
+    else if (p.kind == 2)
+      e = launch_skinny<2>(a, stream);
+    else if (p.bm == 64)
       e = sp ? launch_tile<64, 256, 1, 4, true>(a, stream) : launch_tile<64, 256, 1, 4, false>(a, stream);
     else
       e = sp ? launch_tile<128, 256, 1, 4, true>(a, stream) : launch_tile<128, 256, 1, 4, false>(a, stream);

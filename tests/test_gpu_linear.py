@@ -104,6 +104,34 @@ def test_integer_exact_fp32(gpu_lib, kernel, M):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 300, 1024), (64, 520, 2048), (100, 256, 4096), (128, 1000, 768),
+                                   (129, 300, 640), (300, 300, 1152), (257, 513, 384), (200, 256, 4096),
+                                   (520, 1000, 2048)])
+def test_dense_large_m(gpu_lib, M, N, K):
+    """Dense products (no CSR) above the decode range: ragged M and N, even and odd
+    numbers of groups, and single output tiles whose K is split."""
+    import torch
+    W = workloads.random_weights(3 * M + N, N, K)
+    L = oracle.quantize_layer(W, 0)
+    x = workloads.random_x(M + 7, M, K)
+    _full_check(gpu_lib, torch, L, x, "gemm", sparse=False, label="dense")
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 300, 1024), (300, 300, 1152), (200, 256, 4096)])
+def test_integer_exact_fp32_dense_large_m(gpu_lib, M, N, K):
+    """The integer-exact case through the dense kernels above the decode range,
+    unsplit and split."""
+    import torch
+    x, q, s, z, _, _, _ = workloads.integer_case(M + K, M, N, K, nnz_per_row=0)
+    L = dict(q=q, s=s, z=z, packed=oracle.pack(q))
+    D = layer_to_dev(dict(L, row_ptr=np.zeros(N + 1, np.int32), col=np.zeros(0, np.int32),
+                          val=np.zeros(0, np.float16)), torch)
+    say(f"[exact dense] M={M} N={N} K={K}")
+    y = run_linear(gpu_lib, to_dev(x, torch), D, kernel="gemm", out_dtype=torch.float32, sparse=False)
+    ref = oracle.linear_ref(x, q, s, z)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 def test_empty_sparse_equals_dense(gpu_lib, kernel):
     import torch
