@@ -33,9 +33,10 @@
 //    then unpacked with five instructions per word as 1024 + q or 1024 + 16q (no
 //    zero-point subtraction per weight); the zero-point and the 1024 bias come off
 //    once per group:  sum (q - z) x = P - (1024 + z) S_even - (64 + z) S_odd.
-//  gemv_stream_kernel: activations are too large for LDS; each group's activations
-//    are prefetched together with its weights and the weights are unpacked to the
-//    exact integers q - z.
+//  gemv_ring_kernel (activations too large for LDS): each group's activations are
+//    prefetched with its weights, in whole-row pieces, and each wave passes them
+//    through an LDS slot of its own into the fragment order of the MFMA. The weights
+//    are unpacked to the exact integers q - z (nine instructions per word).
 //
 // Every global load is unconditional, with its address clamped to valid memory: a
 // load under a divergent branch makes the compiler wait for all outstanding loads
@@ -48,7 +49,8 @@ namespace wq {
 
 constexpr int kGemvWaves = 4;   // KW
 constexpr int kGemvDepth = 8;   // D: groups in flight per lane (128-bit weight loads)
-constexpr int kGemvDepthX = 4;  // D when each group also carries its activations
+constexpr int kGemvRingDepth = 4;  // D of gemv_ring_kernel
+constexpr int kNumCu = 256;
 constexpr int kGemvEarly = 8;   // weight groups issued before the wait on staged data
 constexpr int kXLdsMaxHalves = 32768;
 // SZV value of gemv_lds_kernel for scales and zero-points held in registers (see below)
@@ -178,31 +180,48 @@ struct Windows {
   __device__ int next(int b, int gs) const { return b + 1 < nfull ? gs + D : ng - D; }
 };
 
-// Fixed-order sum of the KW partial tiles through LDS and the single store.
-template <int KW>
-__device__ __forceinline__ void reduce_store(f32x4 acc, int wave, int lane, int m0, int mrows, int n, int N,
-                                             void* y, int y_f32) {
+// Fixed-order sum of the KW partial tiles through LDS and the single store; with NT
+// tiles per wave, tile j holds output channel n + 16j.
+template <int KW, int NT>
+__device__ __forceinline__ void reduce_store_tiles(f32x4 (&acc)[NT], int wave, int lane, int m0, int mrows, int n,
+                                                   int N, void* y, int y_f32) {
   if constexpr (KW > 1) {
-    __shared__ f32x4 red[KW - 1][64];
-    if (wave > 0) red[wave - 1][lane] = acc;
+    __shared__ f32x4 red[KW - 1][NT][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) red[wave - 1][j][lane] = acc[j];
+    }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int w = 0; w < KW - 1; ++w) acc += red[w][lane];
+    for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] += red[w][j][lane];
   }
-  if (n >= N) return;
   const int h = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * h + i;
-    if (m < mrows) {
-      const size_t o = (size_t)(m0 + m) * N + n;
-      if (y_f32)
-        static_cast<float*>(y)[o] = acc[i];
-      else
-        static_cast<f16*>(y)[o] = (f16)acc[i];
+  for (int j = 0; j < NT; ++j) {
+    const int nj = n + 16 * j;
+    if (nj >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * h + i;
+      if (m < mrows) {
+        const size_t o = (size_t)(m0 + m) * N + nj;
+        if (y_f32)
+          static_cast<float*>(y)[o] = acc[j][i];
+        else
+          static_cast<f16*>(y)[o] = (f16)acc[j][i];
+      }
     }
   }
+}
+
+template <int KW>
+__device__ __forceinline__ void reduce_store(f32x4 acc, int wave, int lane, int m0, int mrows, int n, int N,
+                                             void* y, int y_f32) {
+  f32x4 a[1] = {acc};
+  reduce_store_tiles<KW, 1>(a, wave, lane, m0, mrows, n, N, y, y_f32);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,99 +431,140 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-template <int KW, int D, int SZV>
+// Each wave passes the activations of each of its groups through a slot of LDS of
+// its own, right before use: the staging loads read whole rows (16 lanes x 16 bytes
+// cover one row's 256 bytes of a group, four rows per load), where the fragment
+// order of the MFMA would need four scattered 16-byte pieces per row and step.
+// Rows of the slot are 272 bytes apart, so the 16 rows of a fragment read fall in
+// distinct banks. One wave writes and reads its slot, and LDS instructions of a
+// wave execute in order, so no barrier is involved.
+template <int KW, int D, int XL, int NT, int SZV>
 __global__ void __launch_bounds__(64 * KW)
-gemv_stream_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
-                   const f16* __restrict__ scales, const f16* __restrict__ zeros, int N,
-                   const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-                   const f16* __restrict__ val, void* __restrict__ y, int y_f32) {
+gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
+                 const f16* __restrict__ scales, const f16* __restrict__ zeros, int N,
+                 const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+                 const f16* __restrict__ val, void* __restrict__ y, int y_f32) {
   constexpr int T = 64 * KW;
+  constexpr int R = 4 * XL;          // rows staged per group
+  constexpr int kRowHalves = 136;    // 128 + 8
   extern __shared__ __align__(16) char smem[];
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, in a scalar register
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r = lane & 15, h = lane >> 4;
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const int n0 = blockIdx.x * 16 * NT, m0 = blockIdx.y * 16;
   const int G = K >> 7;
   const int mrows = min(16, M - m0);
-  f16x2* sz = reinterpret_cast<f16x2*>(smem);  // [16][G + 1]: (s, 1024 + z)
+  f16x2* sz = reinterpret_cast<f16x2*>(smem);  // NT x [16][G + 1]: (s, 1024 + z)
+  f16* slot = reinterpret_cast<f16*>(smem + (size_t)NT * 16 * (G + 1) * 4) + wave * (R * kRowHalves);
 
-  const int n_ld = min(n0 + r, N - 1);
-  const uint32_t* wrow = packed + (size_t)n_ld * (size_t)(K >> 3) + 4 * h;
+  const uint32_t* wrow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    wrow[j] = packed + (size_t)min(n0 + 16 * j + r, N - 1) * (size_t)(K >> 3) + 4 * h;
   const int g_lo = (G * wave) / KW, g_hi = (G * (wave + 1)) / KW;
   const int ng = g_hi - g_lo;
-  const int xr = min(r, mrows - 1);
-  const f16* xrow = x + (size_t)(m0 + xr) * K + 32 * h;
+  // staging: lane (h, r) loads chunk r (input channels 8r .. 8r+7 of a group) of
+  // rows h, h + 4, ..., h + 4(XL-1); rows past M repeat the last row
+  const f16* xst[XL];
+#pragma unroll
+  for (int j = 0; j < XL; ++j) xst[j] = x + (size_t)(m0 + min(h + 4 * j, mrows - 1)) * K + 8 * r;
 
-  SzStage<SZV, T> szs;
-  szs.load(scales, zeros, n0, N, G, t);
-  // each group's activations travel with its weights (same prefetch unit, same order)
+  SzStage<SZV, T> szs[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) szs[j].load(scales, zeros, min(n0 + 16 * j, N - 1), N, G, t);
   const int g_first_valid = min(g_lo, G - 1);
-  uint4 wbuf[D];
-  uint4 xbuf[D][4];
+  uint4 wbuf[D][NT];
+  uint4 xbuf[D][XL];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int g = max(min(g_lo + i, g_hi - 1), g_first_valid);
-    wbuf[i] = *reinterpret_cast<const uint4*>(wrow + (size_t)g * 16);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) xbuf[i][tt] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * 128 + 8 * tt);
+    for (int j = 0; j < NT; ++j) wbuf[i][j] = *reinterpret_cast<const uint4*>(wrow[j] + (size_t)g * 16);
+#pragma unroll
+    for (int j = 0; j < XL; ++j) xbuf[i][j] = *reinterpret_cast<const uint4*>(xst[j] + (size_t)g * 128);
   }
-  szs.store(sz, scales, zeros, n0, N, G, t);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) szs[j].store(sz + j * 16 * (G + 1), scales, zeros, min(n0 + 16 * j, N - 1), N, G, t);
   __syncthreads();
 
   const f16x2* szr = sz + r * (G + 1);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto group = [&](const uint4& w, const uint4* xg, int g) {
-    const f16x2 sbz = szr[g];
-    const f16x2 bias = {sbz[1], sbz[1]};
-    const uint32_t wds[4] = {w.x, w.y, w.z, w.w};
-    f32x4 part = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t magic = magic_1024x2();
+  const f16* frag = slot + min(r, R - 1) * kRowHalves + 32 * h;
+  f32x4 acc[NT];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      part = mfma_16x16x32(as_f16x8(perm_x8(xg[tt])), codes_minus_zero(wds[tt], bias), part);
-    acc += (float)sbz[0] * part;
-    hold_accumulator(part, acc);
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto group = [&](const uint4* w, const uint4* xg, int g) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) *reinterpret_cast<uint4*>(slot + (h + 4 * j) * kRowHalves + 8 * r) = perm_x8(xg[j]);
+    uint4 xa[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) xa[tt] = *reinterpret_cast<const uint4*>(frag + 8 * tt);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const f16x2 sbz = szr[j * 16 * (G + 1) + g];
+      const f16x2 bias = {sbz[1], sbz[1]};
+      const f16 nb = (f16)960.0f - sbz[1];  // -(64 + z)
+      const f16x2 nbias16 = {nb, nb};
+      const uint32_t wds[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+      f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        part = mfma_16x16x32(as_f16x8(xa[tt]), as_f16x8(codes_minus_zero_x16(wds[tt], magic, bias, nbias16)), part);
+      acc[j] += (float)sbz[0] * part;
+      hold_accumulator(part, acc[j]);
+    }
   };
 
   const Windows win(ng, D);
   int gs = 0;
   for (int b = 0; b + 1 < win.n; ++b) {
     const int gs_next = win.next(b, gs);
-    const uint32_t* wn = wrow + (size_t)(g_lo + gs_next) * 16;
-    const f16* xn = xrow + (size_t)(g_lo + gs_next) * 128;
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       group(wbuf[i], xbuf[i], g_lo + gs + i);
-      wbuf[i] = *reinterpret_cast<const uint4*>(wn + i * 16);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) xbuf[i][tt] = *reinterpret_cast<const uint4*>(xn + i * 128 + 8 * tt);
+      for (int j = 0; j < NT; ++j)
+        wbuf[i][j] = *reinterpret_cast<const uint4*>(wrow[j] + (size_t)(g_lo + gs_next + i) * 16);
+#pragma unroll
+      for (int j = 0; j < XL; ++j)
+        xbuf[i][j] = *reinterpret_cast<const uint4*>(xst[j] + (size_t)(g_lo + gs_next + i) * 128);
       __builtin_amdgcn_sched_barrier(kSchedKeepGroups);  // keep the refill next to its consumption
     }
     gs = gs_next;
   }
+  if (win.last_lo == 0 && win.last_hi == D) {
 #pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (i >= win.last_lo && i < win.last_hi) group(wbuf[i], xbuf[i], g_lo + gs + i);
+    for (int i = 0; i < D; ++i) group(wbuf[i], xbuf[i], g_lo + gs + i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i >= win.last_lo && i < win.last_hi) group(wbuf[i], xbuf[i], g_lo + gs + i);
+  }
 
-  const int n = n0 + r;
-  if (row_ptr != nullptr && n < N) {
-    const int e1 = row_ptr[n + 1];
-    for (int e = row_ptr[n] + wave; e < e1; e += KW) {
-      const int c = col[e];
-      const float v = (float)val[e];
+  if (row_ptr != nullptr) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = min(4 * h + i, mrows - 1);
-        acc[i] += v * (float)x[(size_t)(m0 + m) * K + c];
+    for (int j = 0; j < NT; ++j) {
+      const int n = n0 + 16 * j + r;
+      if (n >= N) continue;
+      const int e1 = row_ptr[n + 1];
+      for (int e = row_ptr[n] + wave; e < e1; e += KW) {
+        const int c = col[e];
+        const float v = (float)val[e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = min(4 * h + i, mrows - 1);
+          acc[j][i] += v * (float)x[(size_t)(m0 + m) * K + c];
+        }
       }
     }
   }
-  reduce_store<KW>(acc, wave, lane, m0, mrows, n, N, y, y_f32);
+  reduce_store_tiles<KW, NT>(acc, wave, lane, m0, mrows, n0 + r, N, y, y_f32);
 }
 
 // ---------------------------------------------------------------------------
 template <typename Kern>
-static hipError_t launch_rows(Kern kern, size_t lds, const uint16_t* x, int64_t M, int64_t K,
+static hipError_t launch_rows(Kern kern, size_t lds, int cols, const uint16_t* x, int64_t M, int64_t K,
                               const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N,
                               const int32_t* row_ptr, const int32_t* col, const uint16_t* val, void* y, int y_f32,
                               hipStream_t stream, size_t* lds_set) {
@@ -518,7 +578,7 @@ static hipError_t launch_rows(Kern kern, size_t lds, const uint16_t* x, int64_t 
   const size_t ysz = y_f32 ? 4 : 2;
   for (int64_t m = 0; m < M; m += kRowsPerLaunch) {
     const int64_t mc = M - m < kRowsPerLaunch ? M - m : kRowsPerLaunch;
-    const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((mc + 15) / 16));
+    const dim3 grid((unsigned)((N + cols - 1) / cols), (unsigned)((mc + 15) / 16));
     hipLaunchKernelGGL(kern, grid, dim3(64 * kGemvWaves), lds, stream, reinterpret_cast<const f16*>(x) + m * K,
                        (int)mc, (int)K, packed, reinterpret_cast<const f16*>(scales),
                        reinterpret_cast<const f16*>(zeros), (int)N, row_ptr, col, reinterpret_cast<const f16*>(val),
@@ -537,18 +597,18 @@ static hipError_t launch_lds(const uint16_t* x, int64_t M, int64_t K, const uint
   const int64_t G = K / kGroup, mrows = M < 16 ? M : 16, SR = MR == 1 ? 1 : 4 * ((mrows + 3) / 4);
   const size_t lds = (SZV == kSzInRegs ? 0 : (size_t)16 * (G + 1) * 4) + (size_t)mrows * K * 2 +
                      (size_t)2 * G * SR * 4;
-  return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR>, lds, x, M, K, packed, scales, zeros, N,
+  return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR>, lds, 16, x, M, K, packed, scales, zeros, N,
                      row_ptr, col, val, y, y_f32, stream, &lds_set);
 }
 
-template <int SZV>
-static hipError_t launch_stream(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
-                                const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
-                                const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
+template <int XL, int NT, int SZV>
+static hipError_t launch_ring(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
+                              const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
+                              const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
   static size_t lds_set = 0;
-  const size_t lds = (size_t)16 * (K / kGroup + 1) * 4;
-  return launch_rows(gemv_stream_kernel<kGemvWaves, kGemvDepthX, SZV>, lds, x, M, K, packed, scales, zeros, N,
-                     row_ptr, col, val, y, y_f32, stream, &lds_set);
+  const size_t lds = (size_t)NT * 16 * (K / kGroup + 1) * 4 + (size_t)kGemvWaves * 4 * XL * 136 * 2;
+  return launch_rows(gemv_ring_kernel<kGemvWaves, kGemvRingDepth, XL, NT, SZV>, lds, 16 * NT, x, M, K, packed,
+                     scales, zeros, N, row_ptr, col, val, y, y_f32, stream, &lds_set);
 }
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
@@ -570,21 +630,37 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   // activations fit in LDS next to the scales: stage them once per block, with the
   // fewest staging registers that cover them
   const int64_t xloads = (mrows_max * K / 8 + 64 * kGemvWaves - 1) / (64 * kGemvWaves);
-  const int xc = mrows_max * K > kXLdsMaxHalves ? 0
+  // (from M = 3 on, staging per wave and group is faster, even where x would fit)
+  const int xc = mrows_max * K > kXLdsMaxHalves || mrows_max > 2 ? 0
                  : xloads <= 1 ? 1 : xloads <= 2 ? 2 : xloads <= 4 ? 4 : xloads <= 8 ? 8 : 16;
 #define WQ_ARGS x, M, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, stream
 #define WQ_LDS(XC, SV, MR) \
   if (xc == XC && sz_mode == SV && mr == MR) return launch_lds<XC, SV, MR>(WQ_ARGS)
-#define WQ_LDS_MR(XC, SV) WQ_LDS(XC, SV, 1); WQ_LDS(XC, SV, 2); WQ_LDS(XC, SV, 4)
+#define WQ_LDS_MR(XC, SV) WQ_LDS(XC, SV, 1); WQ_LDS(XC, SV, 2)
   WQ_LDS_MR(1, kSzInRegs); WQ_LDS_MR(2, kSzInRegs); WQ_LDS_MR(4, kSzInRegs); WQ_LDS_MR(8, kSzInRegs);
   WQ_LDS_MR(16, kSzInRegs);
   WQ_LDS_MR(1, 8); WQ_LDS_MR(2, 8); WQ_LDS_MR(4, 8); WQ_LDS_MR(8, 8); WQ_LDS_MR(16, 8);
   WQ_LDS_MR(1, 1); WQ_LDS_MR(2, 1); WQ_LDS_MR(4, 1); WQ_LDS_MR(8, 1); WQ_LDS_MR(16, 1);
   WQ_LDS_MR(1, 0); WQ_LDS_MR(2, 0); WQ_LDS_MR(4, 0); WQ_LDS_MR(8, 0); WQ_LDS_MR(16, 0);
 #undef WQ_LDS_MR
-  if (sv == 8) return launch_stream<8>(WQ_ARGS);
-  if (sv == 1) return launch_stream<1>(WQ_ARGS);
-  return launch_stream<0>(WQ_ARGS);
+  const int xl = mrows_max <= 4 ? 1 : (mrows_max <= 8 ? 2 : 4);
+  // two 16-channel tiles per wave share each staged activation fragment, as long as
+  // the grid still has a block for every CU
+  const int nt = ((N + 31) / 32) * ((M + 15) / 16) >= kNumCu ? 2 : 1;
+#define WQ_RING(XL, NT) \
+  if (xl == XL && nt == NT) { \
+    if (sv == 8) return launch_ring<XL, NT, 8>(WQ_ARGS); \
+    if (sv == 1) return launch_ring<XL, NT, 1>(WQ_ARGS); \
+    return launch_ring<XL, NT, 0>(WQ_ARGS); \
+  }
+  WQ_RING(1, 1);
+  WQ_RING(2, 1);
+  WQ_RING(4, 1);
+  WQ_RING(1, 2);
+  WQ_RING(2, 2);
+  WQ_RING(4, 2);
+#undef WQ_RING
+  return hipErrorInvalidValue;  // not reached
 #undef WQ_LDS
 #undef WQ_ARGS
 }

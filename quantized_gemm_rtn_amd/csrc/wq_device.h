@@ -118,6 +118,19 @@ __device__ __forceinline__ uint4 dequant_word_x16(uint32_t w, uint32_t magic, f1
   return uint4{as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3)};
 }
 
+// Exact fp16 (q - z) for the eight codes of a word, in the order of perm_x8, from the
+// five-instruction unpacking: (1024 + q) - (1024 + z) and (1024 + 16q) / 16 - (64 + z)
+// (nine instructions; bias = 1024 + z, nbias16 = -(64 + z) in both halves).
+__device__ __forceinline__ uint4 codes_minus_zero_x16(uint32_t w, uint32_t magic, f16x2 bias, f16x2 nbias16) {
+  const uint4 b = codes_biased_x16(w, magic);
+  const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 a0 = as_f16x2(b.x) - bias;
+  const f16x2 a1 = __builtin_elementwise_fma(as_f16x2(b.y), sixteenth, nbias16);
+  const f16x2 a2 = as_f16x2(b.z) - bias;
+  const f16x2 a3 = __builtin_elementwise_fma(as_f16x2(b.w), sixteenth, nbias16);
+  return uint4{as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3)};
+}
+
 // Slot of element j (0..7) of a chunk of eight after perm_x8.
 __device__ __forceinline__ int perm_slot(int j) { return ((j & 3) << 1) | (j >> 2); }
 
