@@ -95,8 +95,11 @@ int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* 
 
 /* Bytes of device workspace with which the linear entry points may split the K
  * dimension of the prefill GEMM across blocks (fp32 partial sums, reduced in a
- * fixed order), for shapes whose output tiles alone cannot fill the GPU. 0 when no
- * split is planned. A call given less (or NULL) runs unsplit: same results, slower. */
+ * fixed order), for shapes whose output tiles alone cannot fill the GPU, and, for a
+ * product with a CSR term, hold the activations transposed ([K, M rounded up to 8]
+ * fp16) so that the sparse term joins that fixed-order sum. 0 when no split is
+ * planned. A call given less (or NULL) runs unsplit: same results up to rounding
+ * order, slower. */
 size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*

@@ -759,19 +759,142 @@ splitk_reduce_kernel(const float* __restrict__ ws, int S, size_t MN, void* __res
   }
 }
 
+// x [M][K] -> xt [K][Mp] (Mp: M rounded up to 8; rows M .. Mp-1 of xt are zero), in
+// 64 x 64 tiles through LDS. The sparse term then reads, for an entry in input
+// channel c, the activations of all rows as one contiguous run xt[c][0 .. M).
+__global__ void __launch_bounds__(256) transpose_x_kernel(const f16* __restrict__ x, int M, int K,
+                                                          f16* __restrict__ xt, int Mp) {
+  __shared__ uint32_t tile[64][33];  // 64 rows x 64 halves, rows 33 dwords apart
+  const int t = threadIdx.x;
+  const int k0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = t + 256 * i;
+    const int row = q >> 3, ch = q & 7;
+    const int m = m0 + row;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (m < M) v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + k0 + 8 * ch);
+    tile[row][4 * ch] = v.x;
+    tile[row][4 * ch + 1] = v.y;
+    tile[row][4 * ch + 2] = v.z;
+    tile[row][4 * ch + 3] = v.w;
+  }
+  __syncthreads();
+  const uint16_t* th = reinterpret_cast<const uint16_t*>(&tile[0][0]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = t + 256 * i;
+    const int kk = q >> 3, mc = q & 7;
+    const int m = m0 + 8 * mc;
+    if (m >= Mp) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)th[(8 * mc + 2 * j) * 66 + kk] | ((uint32_t)th[(8 * mc + 2 * j + 1) * 66 + kk] << 16);
+    *reinterpret_cast<uint4*>(xt + (size_t)(k0 + kk) * Mp + m) = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// VM consecutive fp16 values as floats (VM = 1, 2, 4, 8; p aligned to 2 VM bytes)
+template <int VM>
+__device__ __forceinline__ void load_halves(const f16* p, float (&o)[VM]) {
+  if constexpr (VM == 8) {
+    const f16x8 v = as_f16x8(*reinterpret_cast<const uint4*>(p));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (float)v[j];
+  } else if constexpr (VM == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const f16x2 a = as_f16x2(u.x), b = as_f16x2(u.y);
+    o[0] = (float)a[0]; o[1] = (float)a[1]; o[2] = (float)b[0]; o[3] = (float)b[1];
+  } else if constexpr (VM == 2) {
+    const f16x2 a = as_f16x2(*reinterpret_cast<const uint32_t*>(p));
+    o[0] = (float)a[0]; o[1] = (float)a[1];
+  } else {
+    o[0] = (float)p[0];
+  }
+}
+
+// y = sum of the S fp32 K-slices + W_sparse x, for NC output channels per block and
+// all rows in chunks of 64 VM. Sparse term: wave w takes channels n0 + w and
+// n0 + w + 8; each lane holds VM rows and adds, for every CSR entry (c, v) of the
+// channel in order, v * xt[c][rows] (eight entries' loads in flight at once).
+// The per-(row, channel) sums pass through LDS to the fixed-order slice sum.
+template <int VM>
+__global__ void __launch_bounds__(512)
+splitk_sparse_reduce_kernel(const float* __restrict__ ws, int S, int M, int N, const f16* __restrict__ xt, int Mp,
+                            const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+                            const f16* __restrict__ val, void* __restrict__ y, int y_f32) {
+  constexpr int NC = 16, MC = 64 * VM, NW = 8;
+  __shared__ float sp[NC][MC + 1];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n0 = blockIdx.x * NC;
+  const size_t MN = (size_t)M * N;
+  for (int mb = 0; mb < M; mb += MC) {
+    const int mrow = mb + VM * lane;
+    const int mr = mrow < Mp ? mrow : 0;  // lanes past the padded rows read row 0
+#pragma unroll
+    for (int cc = 0; cc < NC / NW; ++cc) {
+      const int nl = wave + NW * cc;
+      const int n = n0 + nl;
+      float acc[VM];
+#pragma unroll
+      for (int j = 0; j < VM; ++j) acc[j] = 0.f;
+      if (n < N) {
+        const int e0 = row_ptr[n], e1 = row_ptr[n + 1];
+        for (int e = e0; e < e1; e += 8) {
+          float xv[8][VM], v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int ec = min(e + u, e1 - 1);
+            v[u] = (float)val[ec];
+            load_halves<VM>(xt + (size_t)col[ec] * Mp + mr, xv[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < VM; ++j) acc[j] = e + u < e1 ? acc[j] + v[u] * xv[u][j] : acc[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < VM; ++j) sp[nl][VM * lane + j] = acc[j];
+    }
+    __syncthreads();
+    for (int q = t; q < MC * NC; q += 64 * NW) {
+      const int nl = q % NC, ml = q / NC;
+      const int m = mb + ml, n = n0 + nl;
+      if (m < M && n < N) {
+        const size_t o = (size_t)m * N + n;
+        float v = ws[o];
+        for (int s2 = 1; s2 < S; ++s2) v += ws[(size_t)s2 * MN + o];
+        v += sp[nl][ml];
+        if (y_f32)
+          static_cast<float*>(y)[o] = v;
+        else
+          static_cast<f16*>(y)[o] = (f16)v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 struct GemmPlan {
   int bm, bn;
   int kind;  // 0: gemm_kernel, 1: gemm_big_kernel 256 x 256, 2: gemm_big_kernel 64 x 256
   int ksplit, k_per_slice;
+  // the sparse term is added in the slice sum, from activations transposed into the
+  // workspace, instead of inside gemm_kernel
+  bool sparse_in_reduce;
 };
 
 // Tile and split choice for M x N x K (shared by the launcher and the workspace query).
 // Dense products take gemm_big_kernel above M = 128 (an even number of groups) and
 // gemm_skinny_kernel for M <= 64 (a multiple of four groups); the others (and every
 // product with a CSR term) take gemm_kernel.
-static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
+static GemmPlan plan_gemm_kind(int64_t M, int64_t N, int64_t K, bool sparse) {
   GemmPlan p;
   const int64_t G = K / 128;
+  p.sparse_in_reduce = false;
   p.kind = sparse ? 0 : (M > 128 && G % 2 == 0 ? 1 : (M <= 64 && G % 4 == 0 ? 2 : 0));
   p.bm = p.kind == 1 ? 256 : (M <= 64 ? 64 : 128);
   p.bn = 256;
@@ -797,14 +920,33 @@ static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
   return p;
 }
 
-static size_t plan_workspace(const GemmPlan& p, int64_t M, int64_t N) {
-  return p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
+static size_t partials_bytes(const GemmPlan& p, int64_t M, int64_t N) {
+  return p.ksplit > 1 ? ((size_t)p.ksplit * M * N * 4 + 255) / 256 * 256 : 0;
+}
+
+static int64_t padded_rows(int64_t M) { return (M + 7) / 8 * 8; }
+
+static size_t plan_workspace(const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
+  return partials_bytes(p, M, N) + (p.sparse_in_reduce ? (size_t)K * padded_rows(M) * 2 : 0);
+}
+
+// A product with a CSR term takes the dense kernel of its shape when that kernel
+// splits K: the sparse term then joins the slice sum.
+static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
+  if (sparse) {
+    GemmPlan d = plan_gemm_kind(M, N, K, false);
+    if (d.kind != 0 && d.ksplit > 1) {
+      d.sparse_in_reduce = true;
+      return d;
+    }
+  }
+  return plan_gemm_kind(M, N, K, sparse);
 }
 
 // enough for the dense and the sparse plan of the shape
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const size_t a = plan_workspace(plan_gemm(M, N, K, false), M, N);
-  const size_t b = plan_workspace(plan_gemm(M, N, K, true), M, N);
+  const size_t a = plan_workspace(plan_gemm(M, N, K, false), M, N, K);
+  const size_t b = plan_workspace(plan_gemm(M, N, K, true), M, N, K);
   return a > b ? a : b;
 }
 
@@ -863,10 +1005,24 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     const int64_t mc = M - m < kRowsPerLaunch ? M - m : kRowsPerLaunch;
     const bool sp = row_ptr != nullptr;
     GemmPlan p = plan_gemm(mc, N, K, sp);
-    const size_t need = plan_workspace(p, mc, N);
+    if (p.sparse_in_reduce && (workspace == nullptr || workspace_bytes < plan_workspace(p, mc, N, K)))
+      p = plan_gemm_kind(mc, N, K, true);  // too small a workspace: the sparse term inside gemm_kernel
+    const size_t need = plan_workspace(p, mc, N, K);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
       p.ksplit = 1;  // no (or too small) workspace: run unsplit
       p.k_per_slice = (int)K;
+    }
+    const bool sp_kernel = sp && !p.sparse_in_reduce;  // sparse term inside gemm_kernel
+    const int64_t Mp = padded_rows(mc);
+    f16* xt = p.sparse_in_reduce
+                  ? reinterpret_cast<f16*>(static_cast<char*>(workspace) + partials_bytes(p, mc, N))
+                  : nullptr;
+    if (p.sparse_in_reduce) {
+      const dim3 tgrid((unsigned)(K / 64), (unsigned)((mc + 63) / 64));
+      hipLaunchKernelGGL(transpose_x_kernel, tgrid, dim3(256), 0, stream, reinterpret_cast<const f16*>(x) + m * K,
+                         (int)mc, (int)K, xt, (int)Mp);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
     const size_t ysz = y_f32 ? 4 : 2;
     GemmArgs a;
@@ -874,10 +1030,10 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.packed = packed;
     a.scales = reinterpret_cast<const f16*>(scales);
     a.zeros = reinterpret_cast<const f16*>(zeros);
-    a.row_ptr = row_ptr;
+    a.row_ptr = sp_kernel ? row_ptr : nullptr;
     a.col = col;
     a.val = reinterpret_cast<const f16*>(val);
-    a.nnz = row_ptr != nullptr ? nnz : 0;
+    a.nnz = sp_kernel ? nnz : 0;
     void* yout = static_cast<char*>(y) + (size_t)(m * N) * ysz;
     a.y = p.ksplit > 1 ? workspace : yout;
     a.M = (int)mc;
@@ -892,11 +1048,26 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     else if (p.kind == 2)
       e = launch_skinny<2>(a, stream);
     else if (p.bm == 64)
-      e = sp ? launch_tile<64, 256, 1, 4, true>(a, stream) : launch_tile<64, 256, 1, 4, false>(a, stream);
+      e = sp_kernel ? launch_tile<64, 256, 1, 4, true>(a, stream) : launch_tile<64, 256, 1, 4, false>(a, stream);
     else
-      e = sp ? launch_tile<128, 256, 1, 4, true>(a, stream) : launch_tile<128, 256, 1, 4, false>(a, stream);
+      e = sp_kernel ? launch_tile<128, 256, 1, 4, true>(a, stream) : launch_tile<128, 256, 1, 4, false>(a, stream);
     if (e != hipSuccess) return e;
-    if (p.ksplit > 1) {
+    if (p.sparse_in_reduce) {
+      const int vm = mc > 256 ? 8 : mc > 128 ? 4 : mc > 64 ? 2 : 1;
+      const dim3 rgrid((unsigned)((N + 15) / 16));
+#define WQ_SPRED(VM)                                                                                         \
+  if (vm == VM)                                                                                              \
+  hipLaunchKernelGGL(splitk_sparse_reduce_kernel<VM>, rgrid, dim3(512), 0, stream,                          \
+                     static_cast<const float*>(workspace), p.ksplit, (int)mc, (int)N, xt, (int)Mp, row_ptr, col, \
+                     reinterpret_cast<const f16*>(val), yout, y_f32)
+      WQ_SPRED(1);
+      WQ_SPRED(2);
+      WQ_SPRED(4);
+      WQ_SPRED(8);
+#undef WQ_SPRED
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else if (p.ksplit > 1) {
       const size_t MN = (size_t)mc * N;
       const int64_t blocks = (int64_t)((MN + 255) / 256) < 4096 ? (int64_t)((MN + 255) / 256) : 4096;
       hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,

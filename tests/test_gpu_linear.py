@@ -132,6 +132,31 @@ def test_integer_exact_fp32_dense_large_m(gpu_lib, M, N, K):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 300, 2048), (64, 520, 2048), (200, 256, 4096), (300, 300, 2304),
+                                   (520, 1000, 2048)])
+def test_sparse_large_m_split(gpu_lib, M, N, K):
+    """CSR products whose dense kernel splits K: the sparse term is added in the
+    slice sum from transposed activations (one or two 512-row chunks)."""
+    import torch
+    W = workloads.random_weights(5 * M + N, N, K)
+    L = oracle.quantize_layer(W, N * K // 200)
+    x = workloads.random_x(M + 11, M, K)
+    _full_check(gpu_lib, torch, L, x, "gemm", label="sparse split")
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 96, 4096), (200, 256, 4096), (520, 300, 2048)])
+def test_integer_exact_fp32_sparse_split(gpu_lib, M, N, K):
+    """The integer-exact case with a CSR term through the split dense kernels."""
+    import torch
+    x, q, s, z, rp, col, val = workloads.integer_case(M + 2 * K, M, N, K, nnz_per_row=5)
+    L = dict(q=q, s=s, z=z, packed=oracle.pack(q), row_ptr=rp, col=col, val=val)
+    D = layer_to_dev(L, torch)
+    say(f"[exact sparse split] M={M} N={N} K={K}")
+    y = run_linear(gpu_lib, to_dev(x, torch), D, kernel="gemm", out_dtype=torch.float32)
+    ref = oracle.linear_ref(x, q, s, z, rp, col, val)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 def test_empty_sparse_equals_dense(gpu_lib, kernel):
     import torch
