@@ -304,33 +304,47 @@ gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense kernel for large M. One block of four waves per compute unit, block tile
-// 256 x 256, wave tile 128 x 128 (4 x 4 subtiles of 32 x 32, accumulators in the
-// accumulation registers). K is consumed in super-steps of one quantization group
-// (128), each split into eight MFMA sub-steps of 16.
-//  - Weights, scales and zero-points of super-step s + 1 are loaded at the start of
-//    super-step s into the other of two register sets, a whole super-step (128
-//    MFMAs per wave) ahead of their use; activations of s + 1 are loaded at the same
-//    time and written to the other of two LDS stages at the end of s.
-//  - Within a super-step the A fragments and dequantized B operands of sub-step
-//    ks + 1 are prepared while the 16 MFMAs of sub-step ks run.
-//  - Lane l = 32h + c of a wave supplies column c of each 32-wide subtile; in
-//    sub-step ks it feeds the eight input channels 64 (ks / 4) + 32h + 8 (ks % 4)
-//    of the group: word 8 (ks / 4) + 4h + ks % 4 of the column's 16 words, so its
-//    weights for the group are two 16-byte loads.
+// Buffer resource of a device array of `bytes` bytes: loads through it take a 32-bit
+// byte offset in a vector register plus one in a scalar register, and loads past the
+// end of the array return zeros (the third-dword value gfx9 expects for raw data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 constexpr int kBigSS = 128;                // halves per super-step (one group)
-constexpr int kBigStride = kBigSS + 8;     // halves per LDS row: 68 dwords, 4 mod 32
+constexpr int kBigStride = kBigSS + 8;     // halves per padded LDS row: 68 dwords, 4 mod 32
 constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 groups x 256 columns
 
+// Dense kernel for large M. As launched: block tile 128 x 256, four waves side by
+// side along N, each 128 x 64 (4 x 2 subtiles of 32 x 32), two blocks per compute
+// unit. The two blocks on a CU meet at their own barriers, so they drift out of
+// phase and each SIMD interleaves one wave's waits with the other's MFMAs. (The
+// template also takes 256 x 256 tiles with eight or four waves, one block per CU.)
+// K is consumed in super-steps of one quantization group (128), each split into
+// eight MFMA sub-steps of 16.
+//  - Weights, scales and zero-points of super-step s + 1 are loaded during the first
+//    half of super-step s into the other of two register sets, a whole super-step
+//    ahead of their use; activations of s + 1 go at the same time straight from
+//    global memory into the other of two LDS stages (buffer loads to LDS), so they
+//    occupy no registers and need no LDS store instructions.
+//  - Within a super-step the A fragments and dequantized B operands of sub-step
+//    ks + 1 are prepared while the MFMAs of sub-step ks run.
+//  - Lane l = 32h + c of a wave supplies column c of each 32-wide subtile; in
+//    sub-step ks it feeds the eight input channels 64 (ks / 4) + 32h + 8 (ks % 4)
+//    of the group (word 8 (ks / 4) + 4h + ks % 4 of the column's 16 words), in
+//    their natural order, matching activations kept in natural order in LDS.
 template <int BM, int BN, int WGM, int WGN, int MINB>
-__global__ void __launch_bounds__(256, MINB)
+__global__ void __launch_bounds__(64 * WGM * WGN, MINB)
 gemm_big_kernel(GemmArgs a) {
+  constexpr int T = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
-  constexpr int XV = BM * (kBigSS / 8) / 256;  // 16-byte activation loads per thread per super-step
-  constexpr int XP = XV / 4;                    // ... per part
-  constexpr int STAGE = BM * kBigStride;
-  static_assert(WGM * WGN == 4 && BN == 256 && XP * 4 == XV && NT <= 4 && MT >= 1, "tile/thread mismatch");
+  constexpr int XV = BM * (kBigSS / 8) / T;  // 16-byte activation loads per thread per super-step
+  constexpr int XP = XV / 4;                  // ... per part
+  constexpr int XR = T / 16;                  // rows between a thread's activation loads
+  constexpr int STAGE = BM * kBigSS;          // rows of 256 bytes, 16-byte chunks swizzled
+  static_assert((T == 256 || T == 512) && BN == 256 && XP * 4 == XV && (NT == 2 || NT == 4) && MT >= NT,
+                "tile/thread mismatch");
 
   extern __shared__ __align__(16) f16 smem[];
   // LDS: two activation stages | (s, z) table szl[buffer][group of the pair][column]
@@ -350,84 +364,109 @@ gemm_big_kernel(GemmArgs a) {
   const int slice = bid / ntile;
   const int tile = bid - slice * ntile;
   const int m0 = (tile % a.tiles_m) * BM, n0 = (tile / a.tiles_m) * BN;
-  const int g0 = slice * (a.k_per_slice >> 7);                  // even
-  const int ng = min(G, g0 + (a.k_per_slice >> 7)) - g0;        // even
+  // (block-uniform values, kept in scalar registers for the loads' scalar offsets)
+  const int g0 = __builtin_amdgcn_readfirstlane(slice * (a.k_per_slice >> 7));            // even
+  const int ng = __builtin_amdgcn_readfirstlane(min(G, g0 + (a.k_per_slice >> 7)) - g0);  // even
 
-  // Offsets are unsigned 32-bit element offsets from the (scalar) base pointers, so
-  // loads take the scalar-base form without 64-bit address arithmetic (M*K and N*K
-  // are below 2^31).
-  // activation producer: thread t loads rows (t >> 4) + 16 i, 16-byte chunk t & 15
-  // (rows beyond M reread row M - 1)
-  const int xch = t & 15, xrow0 = m0 + (t >> 4);
-  const int xdst0 = (t >> 4) * kBigStride + 8 * xch;
-  // weight columns of this lane
-  uint32_t woff[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const uint32_t n = (uint32_t)min(n0 + wn * WTN + 32 * j + c32, N - 1);
-    woff[j] = n * (uint32_t)(K >> 3) + 4 * h;
-  }
-  // (s, z) producer: thread t stages column n0 + t for the two groups of a pair
-  const uint32_t szoff = (uint32_t)min(n0 + t, N - 1) * (uint32_t)G + (uint32_t)g0;
+  // All loads go through buffer resources: a per-lane byte offset fixed for the
+  // whole kernel (row or column) plus a per-super-step scalar offset (the group), so
+  // no address arithmetic is left in the loop. Rows past M and columns past N read
+  // zeros, which only reach outputs that are never stored (M*K and N*K are below
+  // 2^31, so byte offsets fit in 32 bits).
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(a.x, (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(a.packed, (uint32_t)N * (uint32_t)(K >> 1));
+  const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(a.scales, (uint32_t)N * (uint32_t)G * 2u);
+  const __amdgpu_buffer_rsrc_t zrs = buffer_rsrc(a.zeros, (uint32_t)N * (uint32_t)G * 2u);
+  // activations go straight from global memory to LDS: load i of wave w fills the
+  // 1 KB block b = i (T / 64) + w of a stage, rows 4b .. 4b + 3, lane l the 16 bytes
+  // at position l & 15 of row 4b + (l >> 4). Chunk c (input channels 8c .. 8c + 7 of
+  // the group) of row r sits at position c ^ (r & 15), so the 16 rows of a fragment
+  // read fall in distinct banks. Rows beyond M reread row M - 1.
+  const int xrow_l = 4 * wave + (lane >> 4);  // row in block 0; + XR i for load i
+  const int xch = (lane & 15) ^ (xrow_l & 15);
+  const uint32_t xvo = ((uint32_t)(m0 + xrow_l) * (uint32_t)K + 8u * (uint32_t)xch) * 2u;
+  const uint32_t xstep = (uint32_t)XR * (uint32_t)K * 2u;
+  // weights: load I of a super-step (I < 2 NT) gives lane 16q + c the 16 bytes q
+  // (words 4q .. 4q+3) of column 16 I + c of the wave's tile, so one load reads 64
+  // contiguous bytes of each of 16 columns; shuffle_w then moves them into the
+  // lanes of the MFMA B operand
+  const uint32_t wvo = (uint32_t)(n0 + wn * WTN + (lane & 15)) * (uint32_t)(K >> 1) + 16u * (uint32_t)(lane >> 4);
+  const uint32_t wstep = 16u * (uint32_t)(K >> 1);  // 16 columns
+  // (s, z) producer: thread t stages column n0 + (t & 255) for the two groups of a
+  // pair (with 512 threads, two threads write the same value)
+  const int tc = t & 255;
+  const uint32_t szvo = ((uint32_t)(n0 + tc) * (uint32_t)G + (uint32_t)g0) * 2u;
 
   struct WSet {
     uint4 w[NT][2];
   };
   WSet wa, wb;
-  uint4 xr[XV];
   uint32_t sp = 0, zp = 0;  // staged (s, z) of a pair: fp16 pairs (group 2q, 2q + 1)
   // the loads of super-step g in four parts (part p: activation loads XP p ..
-  // XP (p + 1) - 1 and the weights of column subtile p), issued over the first four
-  // sub-steps; the activation stores in four parts over the last four (clamped past
-  // the slice)
-  auto load_part = [&](WSet& W, int g, int p) {
+  // XP (p + 1) - 1 into stage xd, and the weights of loads p NT / 2 ..), issued over
+  // the first four sub-steps (clamped past the slice)
+  auto load_part = [&](WSet& W, f16* xd, int g, int p) {
     const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
-    const uint32_t k0 = 128 * gg + 8 * xch;
-#pragma unroll
-    for (int i = XP * p; i < XP * p + XP; ++i) {
-      const uint32_t row = (uint32_t)min(xrow0 + 16 * i, M - 1);
-      xr[i] = *reinterpret_cast<const uint4*>(a.x + (row * (uint32_t)K + k0));
-    }
-    if (p < NT) {
-      const uint32_t o = woff[p] + 16 * gg;
-      W.w[p][0] = *reinterpret_cast<const uint4*>(a.packed + o);
-      W.w[p][1] = *reinterpret_cast<const uint4*>(a.packed + o + 8);
-    }
-  };
-  auto store_part = [&](f16* st, int p) {
 #pragma unroll
     for (int i = XP * p; i < XP * p + XP; ++i)
-      *reinterpret_cast<uint4*>(st + xdst0 + 16 * i * kBigStride) = perm_x8(xr[i]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (__attribute__((address_space(3))) void*)(xd + (i * (T / 64) + wave) * 512), 16, xvo + i * xstep,
+          (int)(256u * gg), 0, 0);
+#pragma unroll
+    for (int I = p * NT / 2; I < (p + 1) * NT / 2; ++I)
+      W.w[I >> 1][I & 1] =
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo + I * wstep, (int)(64u * gg), 0));
+  };
+  // Loads 2j and 2j + 1 hold columns 32j .. 32j+15 and 32j+16 .. 32j+31 with 16-lane
+  // row q holding words 4q .. 4q+3. The B operand of subtile j wants, in row R of the
+  // wave, (column half R & 1, words 4 (R >> 1) ..) in its first register set and
+  // (column half R & 1, words 8 + 4 (R >> 1) ..) in its second: a swap of odd and
+  // even 16-lane rows between the two loads, then of the 32-lane halves between the
+  // two results, per dword.
+  auto shuffle_w = [&](WSet& W) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      uint32_t* x0 = reinterpret_cast<uint32_t*>(&W.w[j][0]);
+      uint32_t* x1 = reinterpret_cast<uint32_t*>(&W.w[j][1]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto r16 = __builtin_amdgcn_permlane16_swap(x0[d], x1[d], false, false);
+        const auto r32 = __builtin_amdgcn_permlane32_swap(r16[0], r16[1], false, false);
+        x0[d] = r32[0];
+        x1[d] = r32[1];
+      }
+    }
   };
   // (s, z) of the pair starting at super-step g (g even, clamped past the slice)
   auto load_sz = [&](int g) {
-    const uint32_t o = szoff + (uint32_t)min(g, ng - 2);
-    sp = *reinterpret_cast<const uint32_t*>(a.scales + o);
-    zp = *reinterpret_cast<const uint32_t*>(a.zeros + o);
+    const int so = 2 * min(g, ng - 2);
+    sp = __builtin_amdgcn_raw_buffer_load_b32(srs, szvo, so, 0);
+    zp = __builtin_amdgcn_raw_buffer_load_b32(zrs, szvo, so, 0);
   };
   auto store_sz = [&](int buf) {
-    szl[(2 * buf) * 256 + t] = (sp & 0xFFFFu) | (zp << 16);
-    szl[(2 * buf + 1) * 256 + t] = (sp >> 16) | (zp & 0xFFFF0000u);
+    szl[(2 * buf) * 256 + tc] = (sp & 0xFFFFu) | (zp << 16);
+    szl[(2 * buf + 1) * 256 + tc] = (sp >> 16) | (zp & 0xFFFF0000u);
   };
   auto read_sz = [&](uint32_t (&sz)[NT], int buf, int grp) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) sz[j] = szl[(2 * buf + grp) * 256 + wn * WTN + 32 * j + c32];
   };
   const uint32_t magic = magic_1024x2();
+  // A fragment of row r, chunk c = 8 (ks / 4) + 4h + ks % 4 (r & 15 == c32 & 15)
   auto read_a = [&](f16x8 (&av)[MT], const f16* xs, int ks) {
-    const int kk = 64 * (ks >> 2) + 32 * h + 8 * (ks & 3);
+    const int c = (8 * (ks >> 2) + 4 * h + (ks & 3)) ^ (c32 & 15);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      av[i] = *reinterpret_cast<const f16x8*>(xs + (wm * WTM + 32 * i + c32) * kBigStride + kk);
+      av[i] = *reinterpret_cast<const f16x8*>(xs + (wm * WTM + 32 * i + c32) * kBigSS + 8 * c);
   };
+  const f16x2 mul = {(f16)1.0f, (f16)0.0625f};
   auto deq_b = [&](const WSet& W, int j, int ks, uint32_t sz) {
     const f16x2 sz2 = as_f16x2(sz);  // (s, z)
-    const f16 zb = (f16)1024.0f + sz2[1], zn = -((f16)64.0f + sz2[1]);
-    const f16x2 bias = {zb, zb}, nbias16 = {zn, zn}, s2 = {sz2[0], sz2[0]};
+    const f16x2 add = {-((f16)1024.0f + sz2[1]), -((f16)64.0f + sz2[1])}, s2 = {sz2[0], sz2[0]};
     const uint4& q = W.w[j][ks >> 2];
     const int c = ks & 3;
     const uint32_t w = c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
-    return as_f16x8(dequant_word_x16(w, magic, bias, nbias16, s2));
+    return as_f16x8(dequant_word_nat(w, magic, mul, add, s2));
   };
 
   f32x16 acc[MT][NT];
@@ -456,12 +495,12 @@ gemm_big_kernel(GemmArgs a) {
     for (int ks = 0; ks < 8; ++ks) {
       f16x8 (&cur)[MT] = (ks & 1) ? a1 : a0;
       f16x8 (&nxt)[MT] = (ks & 1) ? a0 : a1;
-      if (ks < 4) load_part(Wn, g + 1, ks);
-      if (ks >= 4) store_part(xn, ks - 4);
+      if (ks < 4) load_part(Wn, xn, g + 1, ks);
       if (ks == 0 && pp == 1) load_sz(g + 3);
       if (ks == 4 && pp == 0) store_sz(buf ^ 1);
       if (ks == 6) read_sz(szn, pp == 0 ? buf : buf ^ 1, pp ^ 1);  // the next super-step's
       if (ks < 7) read_a(nxt, xs, ks + 1);
+      if (ks == 7) shuffle_w(Wn);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const f16x8 bnext = j + 1 < NT ? deq_b(W, j + 1, ks, szc[j + 1])
@@ -470,23 +509,8 @@ gemm_big_kernel(GemmArgs a) {
         for (int i = 0; i < MT; ++i) acc[i][j] = mfma_32x32x16(cur[i], bcur, acc[i][j]);
         bcur = bnext;
       }
-      // per column: MFMA, VALU, an LDS read (the A reads of the next sub-step), the
-      // column's share of the loads (sub-steps 0-3) or of the activation stores
-      // (4-7), then (MFMA, VALU) for the column's other row subtiles: about 16 VALU
-      // (the next operand's unpacking) spread over its MT MFMAs
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 16 / MT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (ks < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-        else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-#pragma unroll
-        for (int r = 1; r < MT; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 16 / MT, 0);
-        }
-      }
+      // (two waves per SIMD interleave MFMAs and vector work by themselves; an
+      // explicit per-MFMA interleaving here only cost registers)
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
@@ -502,9 +526,8 @@ gemm_big_kernel(GemmArgs a) {
     store_sz(0);
     load_sz(2);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) load_part(wa, 0, p);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) store_part(smem, p);
+    for (int p = 0; p < 4; ++p) load_part(wa, smem, 0, p);
+    shuffle_w(wa);
     __syncthreads();
     read_a(a0, smem, 0);
     read_sz(szc, 0, 0);
@@ -896,14 +919,14 @@ static GemmPlan plan_gemm_kind(int64_t M, int64_t N, int64_t K, bool sparse) {
   const int64_t G = K / 128;
   p.sparse_in_reduce = false;
   p.kind = sparse ? 0 : (M > 128 && G % 2 == 0 ? 1 : (M <= 64 && G % 4 == 0 ? 2 : 0));
-  p.bm = p.kind == 1 ? 256 : (M <= 64 ? 64 : 128);
+  p.bm = p.kind == 1 ? 128 : (M <= 64 ? 64 : 128);
   p.bn = 256;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   int64_t s = 1;
   if (p.kind != 0) {
-    // split K while the grid is below one (256 x 256) or two (64 x 256) blocks per CU
-    // and each slice keeps >= 8 groups; slices are an even number of groups
-    const int64_t target = p.kind == 1 ? 256 : 512;
+    // split K while the grid is below two blocks per CU and each slice keeps >= 8
+    // groups; slices are a multiple of two (large M) or four (skinny) groups
+    const int64_t target = 512;
     const int64_t groups = K / 128;
     while (tiles * s * 2 <= target && groups / (s * 2) >= 8) s *= 2;
     p.ksplit = (int)s;
@@ -952,7 +975,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 template <int BM, int BN, int WGM, int WGN, int MINB>
 static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
-  constexpr size_t lds = 2 * (size_t)BM * kBigStride * sizeof(f16) + kBigSzBytes;
+  constexpr size_t lds = 2 * (size_t)BM * kBigSS * sizeof(f16) + kBigSzBytes;
   auto kern = gemm_big_kernel<BM, BN, WGM, WGN, MINB>;
   static bool attr_done = false;  // setting the same attribute twice is harmless
   if (!attr_done) {
@@ -964,7 +987,7 @@ static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int64_t nblk = (int64_t)a.tiles_m * a.tiles_n * a.ksplit;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * WGM * WGN), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1044,7 +1067,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.k_per_slice = p.k_per_slice;
     hipError_t e;
     if (p.kind == 1)
-      e = launch_big<256, 256, 2, 2, 1>(a, stream);
+      e = launch_big<128, 256, 1, 4, 2>(a, stream);
     else if (p.kind == 2)
       e = launch_skinny<2>(a, stream);
     else if (p.bm == 64)

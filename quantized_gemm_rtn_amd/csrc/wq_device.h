@@ -131,6 +131,22 @@ __device__ __forceinline__ uint4 codes_minus_zero_x16(uint32_t w, uint32_t magic
   return uint4{as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3)};
 }
 
+// fp16 (q - z) * s for the eight codes of a word in their natural order (q0, q1),
+// (q2, q3), (q4, q5), (q6, q7): byte b of the word copied into both halves, masked
+// to (q_2b, 16 q_2b+1) and biased by 1024, then (1, 1/16) * v + (-(1024 + z),
+// -(64 + z)) is exactly q - z, rounded once in the multiply by s (sixteen
+// instructions). mul = (1, 1/16), add = (-(1024 + z), -(64 + z)), s in both halves.
+__device__ __forceinline__ uint4 dequant_word_nat(uint32_t w, uint32_t magic, f16x2 mul, f16x2 add, f16x2 s) {
+  uint32_t r[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t t = __builtin_amdgcn_perm(w, w, 0x0c000c00u | (0x00010001u * b));
+    const f16x2 v = as_f16x2(and_or(t, 0x00F0000Fu, magic));
+    r[b] = as_u32(__builtin_elementwise_fma(v, mul, add) * s);
+  }
+  return uint4{r[0], r[1], r[2], r[3]};
+}
+
 // Slot of element j (0..7) of a chunk of eight after perm_x8.
 __device__ __forceinline__ int perm_slot(int j) { return ((j & 3) << 1) | (j >> 2); }
 
