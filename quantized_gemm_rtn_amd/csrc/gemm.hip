@@ -333,7 +333,7 @@ constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 gro
 //    sub-step ks it feeds the eight input channels 64 (ks / 4) + 32h + 8 (ks % 4)
 //    of the group (word 8 (ks / 4) + 4h + ks % 4 of the column's 16 words), in
 //    their natural order, matching activations kept in natural order in LDS.
-template <int BM, int BN, int WGM, int WGN, int MINB>
+template <int BM, int BN, int WGM, int WGN, int MINB, int WS>
 __global__ void __launch_bounds__(64 * WGM * WGN, MINB)
 gemm_big_kernel(GemmArgs a) {
   constexpr int T = 64 * WGM * WGN;
@@ -400,20 +400,30 @@ gemm_big_kernel(GemmArgs a) {
   struct WSet {
     uint4 w[NT][2];
   };
-  WSet wa, wb;
+  // weights: 2 WS register sets; the sets of WS consecutive super-steps are loaded
+  // together (WS super-steps ahead of the first of them), so the 64 bytes a column
+  // gives each group come from DRAM as WS neighbouring pieces rather than one piece
+  // per super-step
+  WSet wset[2 * WS];
   uint32_t sp = 0, zp = 0;  // staged (s, z) of a pair: fp16 pairs (group 2q, 2q + 1)
   // the loads of super-step g in four parts (part p: activation loads XP p ..
   // XP (p + 1) - 1 into stage xd, and the weights of loads p NT / 2 ..), issued over
   // the first four sub-steps (clamped past the slice)
-  auto load_part = [&](WSet& W, f16* xd, int g, int p) {
+  // activation loads XP p .. XP (p + 1) - 1 of super-step g into stage xd (clamped
+  // past the slice)
+  auto load_x_part = [&](f16* xd, int g, int p) {
     const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
 #pragma unroll
     for (int i = XP * p; i < XP * p + XP; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrs, (__attribute__((address_space(3))) void*)(xd + (i * (T / 64) + wave) * 512), 16, xvo + i * xstep,
           (int)(256u * gg), 0, 0);
+  };
+  // weight loads I .. I + c - 1 of super-step g into W
+  auto load_w = [&](WSet& W, int g, int I0, int c) {
+    const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
 #pragma unroll
-    for (int I = p * NT / 2; I < (p + 1) * NT / 2; ++I)
+    for (int I = I0; I < I0 + c; ++I)
       W.w[I >> 1][I & 1] =
           __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo + I * wstep, (int)(64u * gg), 0));
   };
@@ -477,26 +487,43 @@ gemm_big_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // One super-step (position pp in its pair, (s, z) table buffer buf): W holds its
-  // weights, Wn receives those of the next one; activations are read from stage xs
-  // and the next ones written to stage xn (last read before the barrier that ended
-  // the previous super-step). The A fragments of sub-step ks + 1 are read during
-  // sub-step ks, and the B operand of the next column (of the next sub-step, or of
-  // the next super-step after the last column) is unpacked during the four MFMAs of
-  // the current one: a wave issues in order, so vector work placed between its MFMAs
-  // runs while the matrix core is busy instead of beside it. The (s, z) of pair q + 1
-  // are loaded in the second super-step of pair q - 1 and staged in the first of
-  // pair q, a barrier before they are first read.
+  // Super-step g = g_window + u (u = 0 .. 2 WS - 1, a constant after unrolling): its
+  // weights are in set u and those of the next one in set u + 1; activations are read
+  // from stage xs and the next ones loaded into stage xn (last read before the
+  // barrier that ended the previous super-step). At u = 0 and u = WS the weights of
+  // the other half of the sets (the next WS super-steps) are loaded. The A fragments
+  // of sub-step ks + 1 are read during sub-step ks, and the B operand of the next
+  // column (of the next sub-step, or of the next super-step after the last column) is
+  // unpacked during the MFMAs of the current one. The (s, z) of pair q + 1 are loaded
+  // in the second super-step of pair q - 1 and staged in the first of pair q, a
+  // barrier before they are first read.
   f16x8 a0[MT], a1[MT];
   f16x8 bcur;
   uint32_t szc[NT], szn[NT];
-  auto superstep = [&](const WSet& W, WSet& Wn, const f16* xs, f16* xn, int g, int pp, int buf) {
+  auto superstep = [&](int u, const f16* xs, f16* xn, int g) {
+    const WSet& W = wset[u];
+    WSet& Wn = wset[(u + 1) % (2 * WS)];
+    const int pp = g & 1, buf = (g >> 1) & 1;
+    constexpr int WPK = WS * 2 * NT / 4;  // weight loads per sub-step 0 .. 3 at a window start
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       f16x8 (&cur)[MT] = (ks & 1) ? a1 : a0;
       f16x8 (&nxt)[MT] = (ks & 1) ? a0 : a1;
-      if (ks < 4) load_part(Wn, xn, g + 1, ks);
+      // (s, z) and activation loads first, weight loads after them: the barrier at the
+      // end then waits for the activations only
       if (ks == 0 && pp == 1) load_sz(g + 3);
+      if (ks == 0) {
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) load_x_part(xn, g + 1, p2);
+      }
+      if (ks < 4 && (u == 0 || u == WS)) {
+        // window loads: super-steps g + WS + v into sets (u + WS + v) mod 2 WS
+#pragma unroll
+        for (int q = ks * WPK; q < (ks + 1) * WPK; ++q) {
+          const int v = q / (2 * NT), I = q % (2 * NT);
+          load_w(wset[(u + WS + v) % (2 * WS)], g + WS + v, I, 1);
+        }
+      }
       if (ks == 4 && pp == 0) store_sz(buf ^ 1);
       if (ks == 6) read_sz(szn, pp == 0 ? buf : buf ^ 1, pp ^ 1);  // the next super-step's
       if (ks < 7) read_a(nxt, xs, ks + 1);
@@ -513,29 +540,42 @@ gemm_big_kernel(GemmArgs a) {
       // explicit per-MFMA interleaving here only cost registers)
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+    {
+      // Stage xn must be complete for every wave before the barrier: wait for this
+      // wave's activation loads (and LDS reads), but not for the weight loads issued
+      // after them, which stay in flight (s_waitcnt: vmcnt in bits 3:0 and 15:14,
+      // expcnt 7 = no wait, lgkmcnt 0). A plain __syncthreads() would wait for all.
+      constexpr int nw = WS * 2 * NT;
+      if (u == 0 || u == WS)
+        __builtin_amdgcn_s_waitcnt((nw & 15) | ((nw >> 4) << 14) | 0x70);
+      else
+        __builtin_amdgcn_s_waitcnt(0x70);
+      __builtin_amdgcn_s_barrier();
+    }
     read_a(a0, xn, 0);
 #pragma unroll
     for (int j = 0; j < NT; ++j) szc[j] = szn[j];
   };
 
   if (ng > 0) {
-    // prologue: (s, z) of pairs 0 (staged) and 1 (in registers), activations and
-    // weights of super-step 0
+    // prologue: (s, z) of pairs 0 (staged) and 1 (in registers), activations of
+    // super-step 0, weights of super-steps 0 .. WS - 1 (ng is a multiple of 2 WS)
     load_sz(0);
     store_sz(0);
     load_sz(2);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) load_part(wa, smem, 0, p);
-    shuffle_w(wa);
+    for (int p = 0; p < 4; ++p) load_x_part(smem, 0, p);
+#pragma unroll
+    for (int v = 0; v < WS; ++v) load_w(wset[v], v, 0, 2 * NT);
+    shuffle_w(wset[0]);
     __syncthreads();
     read_a(a0, smem, 0);
     read_sz(szc, 0, 0);
-    bcur = deq_b(wa, 0, 0, szc[0]);
-    for (int g = 0; g < ng; g += 2) {
-      const int buf = (g >> 1) & 1;
-      superstep(wa, wb, smem, smem + STAGE, g, 0, buf);
-      superstep(wb, wa, smem + STAGE, smem, g + 1, 1, buf);
+    bcur = deq_b(wset[0], 0, 0, szc[0]);
+    for (int g = 0; g < ng; g += 2 * WS) {
+#pragma unroll
+      for (int u = 0; u < 2 * WS; ++u)
+        superstep(u, smem + (u & 1) * STAGE, smem + ((u + 1) & 1) * STAGE, g + u);
     }
   }
 
@@ -903,7 +943,9 @@ splitk_sparse_reduce_kernel(const float* __restrict__ ws, int S, int M, int N, c
 
 struct GemmPlan {
   int bm, bn;
-  int kind;  // 0: gemm_kernel, 1: gemm_big_kernel 256 x 256, 2: gemm_big_kernel 64 x 256
+  // 0: gemm_kernel; 1: gemm_big_kernel 128 x 256; 2 (M <= 64): gemm_big_kernel 64 x 256
+  // with weight windows of four or two super-steps, else gemm_skinny_kernel
+  int kind;
   int ksplit, k_per_slice;
   // the sparse term is added in the slice sum, from activations transposed into the
   // workspace, instead of inside gemm_kernel
@@ -912,8 +954,8 @@ struct GemmPlan {
 
 // Tile and split choice for M x N x K (shared by the launcher and the workspace query).
 // Dense products take gemm_big_kernel above M = 128 (an even number of groups) and
-// gemm_skinny_kernel for M <= 64 (a multiple of four groups); the others (and every
-// product with a CSR term) take gemm_kernel.
+// the M <= 64 kernels for M <= 64 (a multiple of four groups); the others take
+// gemm_kernel (and so does a product with a CSR term unless its kernel splits K).
 static GemmPlan plan_gemm_kind(int64_t M, int64_t N, int64_t K, bool sparse) {
   GemmPlan p;
   const int64_t G = K / 128;
@@ -924,9 +966,11 @@ static GemmPlan plan_gemm_kind(int64_t M, int64_t N, int64_t K, bool sparse) {
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   int64_t s = 1;
   if (p.kind != 0) {
-    // split K while the grid is below two blocks per CU and each slice keeps >= 8
-    // groups; slices are a multiple of two (large M) or four (skinny) groups
-    const int64_t target = 512;
+    // split K while the grid is below two blocks per CU (large M) or one (M <= 64,
+    // where longer slices amortize each block's first loads and partial stores better
+    // than a second block per CU hides latency), and each slice keeps >= 8 groups;
+    // slices are a multiple of two (large M) or four (M <= 64) groups
+    const int64_t target = p.kind == 2 ? 256 : 512;
     const int64_t groups = K / 128;
     while (tiles * s * 2 <= target && groups / (s * 2) >= 8) s *= 2;
     p.ksplit = (int)s;
@@ -973,10 +1017,10 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return a > b ? a : b;
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB>
+template <int BM, int BN, int WGM, int WGN, int MINB, int WS>
 static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
   constexpr size_t lds = 2 * (size_t)BM * kBigSS * sizeof(f16) + kBigSzBytes;
-  auto kern = gemm_big_kernel<BM, BN, WGM, WGN, MINB>;
+  auto kern = gemm_big_kernel<BM, BN, WGM, WGN, MINB, WS>;
   static bool attr_done = false;  // setting the same attribute twice is harmless
   if (!attr_done) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1066,8 +1110,15 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.ksplit = p.ksplit;
     a.k_per_slice = p.k_per_slice;
     hipError_t e;
+    // weight windows of WS super-steps need slices and K of a multiple of 2 WS groups
+    const int64_t per = p.k_per_slice / 128, G = K / 128;
+    const int ws = per % 8 == 0 && G % 8 == 0 ? 4 : (per % 4 == 0 && G % 4 == 0 ? 2 : 1);
     if (p.kind == 1)
-      e = launch_big<128, 256, 1, 4, 2>(a, stream);
+      e = launch_big<128, 256, 1, 4, 2, 1>(a, stream);
+    else if (p.kind == 2 && ws == 4)
+      e = launch_big<64, 256, 1, 4, 2, 4>(a, stream);
+    else if (p.kind == 2 && ws == 2)
+      e = launch_big<64, 256, 1, 4, 2, 2>(a, stream);
     else if (p.kind == 2)
       e = launch_skinny<2>(a, stream);
     else if (p.bm == 64)

@@ -106,7 +106,7 @@ def test_integer_exact_fp32(gpu_lib, kernel, M):
 
 @pytest.mark.parametrize("M,N,K", [(17, 300, 1024), (64, 520, 2048), (100, 256, 4096), (128, 1000, 768),
                                    (129, 300, 640), (300, 300, 1152), (257, 513, 384), (200, 256, 4096),
-                                   (520, 1000, 2048)])
+                                   (520, 1000, 2048), (48, 300, 1536)])
 def test_dense_large_m(gpu_lib, M, N, K):
     """Dense products (no CSR) above the decode range: ragged M and N, even and odd
     numbers of groups, and single output tiles whose K is split."""
@@ -133,7 +133,7 @@ def test_integer_exact_fp32_dense_large_m(gpu_lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 300, 2048), (64, 520, 2048), (200, 256, 4096), (300, 300, 2304),
-                                   (520, 1000, 2048)])
+                                   (520, 1000, 2048), (48, 300, 3072)])
 def test_sparse_large_m_split(gpu_lib, M, N, K):
     """CSR products whose dense kernel splits K: the sparse term is added in the
     slice sum from transposed activations (one or two 512-row chunks)."""
