@@ -66,17 +66,27 @@ constexpr int kSchedKeepGroups = 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x
 // Scale / zero-point staging: LDS sz[16][G + 1] = (s, 1024 + z) for the block's rows.
 // The row stride G + 1 is odd (G is even whenever it matters), so the 16 lanes that
 // read one group of 16 rows hit 16 different banks.
-//   SZV = 8: rows as 16-byte vectors (G % 8 == 0, G <= 256): <= 2 loads per thread
+//   SZV = 8, 4, 2: rows as vectors of SZV halves (G % SZV == 0, so no vector
+//     crosses a row; G <= kSzMaxG): <= 2, 2, 4 loads per thread
 //   SZV = 1: as halves (G <= 256): <= 16 loads per thread
 //   SZV = 0: a plain loop (any G), run after the weight prefetch
+template <int V> struct SzBits;
+template <> struct SzBits<8> { typedef uint4 type; };
+template <> struct SzBits<4> { typedef uint2 type; };
+template <> struct SzBits<2> { typedef uint32_t type; };
+template <> struct SzBits<1> { typedef uint16_t type; };
+template <int V> struct Halves { f16 h[V]; };
+// largest G each vector width is chosen for
+template <int V> constexpr int kSzMaxG = V == 8 || V == 1 ? 256 : 128;
+
 template <int SZV, int T>
 struct SzStage {
-  static constexpr int C = SZV == 8 ? 2 : (SZV == 1 ? 16 : 0);
-  uint4 v8s[SZV == 8 ? C : 1], v8z[SZV == 8 ? C : 1];
-  uint16_t v1s[SZV == 1 ? C : 1], v1z[SZV == 1 ? C : 1];
+  static constexpr int V = SZV > 0 ? SZV : 1;
+  static constexpr int C = SZV == 0 ? 0 : (16 * kSzMaxG<V> / V + T - 1) / T;
+  typedef typename SzBits<V>::type Vec;
+  Vec vs[C > 0 ? C : 1], vz[C > 0 ? C : 1];
 
   __device__ __forceinline__ void load(const f16* scales, const f16* zeros, int n0, int N, int G, int t) {
-    constexpr int V = SZV > 0 ? SZV : 1;
     const int nload = 16 * G / V;
     // the block's 16 rows are contiguous; past row N - 1 the last vector is repeated
     const size_t o0 = (size_t)n0 * G, o_last = (size_t)N * G - V;
@@ -84,13 +94,8 @@ struct SzStage {
     for (int i = 0; i < C; ++i) {
       const int idx = min(t + i * T, nload - 1);
       const size_t o = min(o0 + (size_t)idx * V, o_last);
-      if constexpr (SZV == 8) {
-        v8s[i] = *reinterpret_cast<const uint4*>(scales + o);
-        v8z[i] = *reinterpret_cast<const uint4*>(zeros + o);
-      } else {
-        v1s[i] = __builtin_bit_cast(uint16_t, scales[o]);
-        v1z[i] = __builtin_bit_cast(uint16_t, zeros[o]);
-      }
+      vs[i] = *reinterpret_cast<const Vec*>(scales + o);
+      vz[i] = *reinterpret_cast<const Vec*>(zeros + o);
     }
   }
   // stores are unconditional too (clamped indices rewrite identical values), so the
@@ -98,18 +103,14 @@ struct SzStage {
   __device__ __forceinline__ void store(f16x2* sz, const f16* scales, const f16* zeros, int n0, int N, int G,
                                         int t) {
     const f16 k1024 = (f16)1024.0f;
-    const int nload = 16 * G / (SZV > 0 ? SZV : 1);
+    const int nload = 16 * G / V;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int idx = min(t + i * T, nload - 1);
-      if constexpr (SZV == 8) {
-        const f16x8 s8 = as_f16x8(v8s[i]), z8 = as_f16x8(v8z[i]);
-        const int base = 8 * idx + (8 * idx) / G;  // row * (G + 1) + column
+      const Halves<V> s = __builtin_bit_cast(Halves<V>, vs[i]), z = __builtin_bit_cast(Halves<V>, vz[i]);
+      const int base = V * idx + (V * idx) / G;  // row * (G + 1) + column
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sz[base + j] = f16x2{s8[j], (f16)(k1024 + z8[j])};
-      } else {
-        sz[idx + idx / G] = f16x2{bits_to_f16(v1s[i]), (f16)(k1024 + bits_to_f16(v1z[i]))};
-      }
+      for (int j = 0; j < V; ++j) sz[base + j] = f16x2{s.h[j], (f16)(k1024 + z.h[j])};
     }
     if constexpr (SZV == 0) {
       for (int idx = t; idx < 16 * G; idx += T) {
@@ -616,10 +617,17 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
                        const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
   const int64_t G = K / kGroup;
   const int64_t mrows_max = M < 16 ? M : 16;
-  // scales/zeros rows as 16-byte vectors when every row starts 16-byte aligned
-  const bool vec = G % 8 == 0 && G <= 256 && reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(zeros) % 16 == 0;
-  const int sv = vec ? 8 : (G <= 256 ? 1 : 0);
+  // scales/zeros rows as vectors of 8, 4 or 2 halves when G is a multiple of the
+  // width and every row starts aligned to it
+  const auto aligned = [&](uintptr_t b) {
+    return reinterpret_cast<uintptr_t>(scales) % b == 0 && reinterpret_cast<uintptr_t>(zeros) % b == 0;
+  };
+  const int sv = G % 8 == 0 && G <= kSzMaxG<8> && aligned(16)  ? 8
+                 : G % 4 == 0 && G <= kSzMaxG<4> && aligned(8) ? 4
+                 : G % 2 == 0 && G <= kSzMaxG<2> && aligned(4) ? 2
+                 : G <= kSzMaxG<1>                             ? 1
+                                                               : 0;
+  const bool vec = sv == 8;
   // scales and zero-points in registers, two loads per window of D groups: every
   // wave's window starts on a multiple of D groups
   static_assert(kGemvDepth == 4 || kGemvDepth == 8, "in-register (s, z) windows hold 4 or 8 groups");
@@ -640,6 +648,8 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   WQ_LDS_MR(1, kSzInRegs); WQ_LDS_MR(2, kSzInRegs); WQ_LDS_MR(4, kSzInRegs); WQ_LDS_MR(8, kSzInRegs);
   WQ_LDS_MR(16, kSzInRegs);
   WQ_LDS_MR(1, 8); WQ_LDS_MR(2, 8); WQ_LDS_MR(4, 8); WQ_LDS_MR(8, 8); WQ_LDS_MR(16, 8);
+  WQ_LDS_MR(1, 4); WQ_LDS_MR(2, 4); WQ_LDS_MR(4, 4); WQ_LDS_MR(8, 4); WQ_LDS_MR(16, 4);
+  WQ_LDS_MR(1, 2); WQ_LDS_MR(2, 2); WQ_LDS_MR(4, 2); WQ_LDS_MR(8, 2); WQ_LDS_MR(16, 2);
   WQ_LDS_MR(1, 1); WQ_LDS_MR(2, 1); WQ_LDS_MR(4, 1); WQ_LDS_MR(8, 1); WQ_LDS_MR(16, 1);
   WQ_LDS_MR(1, 0); WQ_LDS_MR(2, 0); WQ_LDS_MR(4, 0); WQ_LDS_MR(8, 0); WQ_LDS_MR(16, 0);
 #undef WQ_LDS_MR
@@ -650,6 +660,8 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
 #define WQ_RING(XL, NT) \
   if (xl == XL && nt == NT) { \
     if (sv == 8) return launch_ring<XL, NT, 8>(WQ_ARGS); \
+    if (sv == 4) return launch_ring<XL, NT, 4>(WQ_ARGS); \
+    if (sv == 2) return launch_ring<XL, NT, 2>(WQ_ARGS); \
     if (sv == 1) return launch_ring<XL, NT, 1>(WQ_ARGS); \
     return launch_ring<XL, NT, 0>(WQ_ARGS); \
   }

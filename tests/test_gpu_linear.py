@@ -104,6 +104,35 @@ def test_integer_exact_fp32(gpu_lib, kernel, M):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("K", [3584, 1536, 2816, 16896])
+@pytest.mark.parametrize("M", [1, 2, 5, 16])
+def test_decode_scale_staging_widths(gpu_lib, M, K):
+    """Decode kernels whose per-group scales and zero-points are staged as vectors
+    of four halves (G = 28, 12), two halves (G = 22) and single halves (G = 132),
+    with a ragged N and a CSR term."""
+    import torch
+    N = 300 if K <= 4096 else 40
+    W = workloads.random_weights(K + M, N, K)
+    L = oracle.quantize_layer(W, N * K // 300)
+    x = workloads.random_x(K + 3 * M, M, K)
+    _full_check(gpu_lib, torch, L, x, "gemv", label="staging widths")
+
+
+@pytest.mark.parametrize("K", [3584, 2816])
+@pytest.mark.parametrize("M", [1, 8])
+def test_integer_exact_fp32_staging_widths(gpu_lib, M, K):
+    """The integer-exact case through the decode kernels at G = 28 and G = 22."""
+    import torch
+    N = 96
+    x, q, s, z, rp, col, val = workloads.integer_case(M + K, M, N, K, nnz_per_row=5)
+    L = dict(q=q, s=s, z=z, packed=oracle.pack(q), row_ptr=rp, col=col, val=val)
+    D = layer_to_dev(L, torch)
+    say(f"[exact staging] M={M} K={K}")
+    y = run_linear(gpu_lib, to_dev(x, torch), D, kernel="gemv", out_dtype=torch.float32)
+    ref = oracle.linear_ref(x, q, s, z, rp, col, val)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(17, 300, 1024), (64, 520, 2048), (100, 256, 4096), (128, 1000, 768),
                                    (129, 300, 640), (300, 300, 1152), (257, 513, 384), (200, 256, 4096),
                                    (520, 1000, 2048), (48, 300, 1536)])
