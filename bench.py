@@ -12,12 +12,14 @@ reported separately under "offline").
 Inputs stay resident in HBM: R copies of the layer (packed codes, scales,
 zeros, CSR, x, y) totalling >= 1 GiB are rotated so no launch is served from
 the 256 MB Infinity Cache.  The K timed launches are captured in one HIP graph
-and replayed once between synchronizations; HIP events on the launch stream
-bracket the replay.
+and replayed five times, each between synchronizations; HIP events on the
+launch stream bracket each replay, and the median replay gives the figures
+(p10 and p90 are reported beside them).
 
 Printed: ONE JSON line with the metric (GB/s, algorithmic bytes), the roofline
 of the dominant kernel, the CPU oracle baseline, and the other workloads
-(batched decode + sparse, prefill, the 70B down-projection M sweep).
+(batched decode + sparse, prefill, the 70B down-projection M sweep and one GPU's
+shard of it), and, as context, torch's device copy of the same byte count.
 """
 from __future__ import annotations
 
@@ -54,8 +56,8 @@ def alg_flops(M, N, K, nnz):
 class Layer:
     """A quantized layer on the GPU, produced by the library's own quantizer."""
 
-    def __init__(self, wq, torch, index, M):
-        W, x, cfg = workloads.make(index, M=M)
+    def __init__(self, wq, torch, index, M, K=None):
+        W, x, cfg = workloads.make(index, M=M, K=K)
         N, K = W.shape
         self.N, self.K, self.M = N, K, M
         self.sparse_k = workloads.sparse_k_for(cfg, N, K)
@@ -87,9 +89,10 @@ def launch(wq, s, kernel="auto"):
                      out=s["y"], kernel=kernel)
 
 
-def time_launches(wq, torch, sets, steps, warmup, kernel="auto"):
+def time_launches(wq, torch, sets, steps, warmup, kernel="auto", repeats=5):
     """Warm up eagerly, capture `steps` rotating launches in one graph, replay it
-    once between synchronizations; returns milliseconds per launch."""
+    `repeats` times, each between synchronizations; returns the milliseconds per
+    launch of every replay."""
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -102,26 +105,31 @@ def time_launches(wq, torch, sets, steps, warmup, kernel="auto"):
     torch.cuda.synchronize()
     g.replay()  # untimed replay: first replay uploads the graph
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
+    per_launch = []
+    for _ in range(repeats):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            start.record(stream)
+            g.replay()
+            end.record(stream)
         torch.cuda.synchronize()
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+        per_launch.append(start.elapsed_time(end) / steps)
     del g
-    return ms / steps
+    return per_launch
 
 
-def measure(wq, torch, index, M, steps, warmup, kernel="auto"):
-    L = Layer(wq, torch, index, M)
+def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None):
+    L = Layer(wq, torch, index, M, K)
     sets = L.sets(torch, ROTATE_BYTES)
-    ms = time_launches(wq, torch, sets, steps, warmup, kernel)
+    runs = time_launches(wq, torch, sets, steps, warmup, kernel)
+    ms = float(np.median(runs))
     nb = alg_bytes(M, L.N, L.K, L.sparse_k)
     nf = alg_flops(M, L.N, L.K, L.sparse_k)
     used = kernel if kernel != "auto" else wq.auto_kernel(M, L.N, L.K)
     res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, kernel=used, us_per_launch=ms * 1e3,
+               us_p10=float(np.percentile(runs, 10)) * 1e3, us_p90=float(np.percentile(runs, 90)) * 1e3,
+               replays=len(runs),
                alg_bytes=nb, alg_flops=nf, GBps=nb / (ms * 1e-3) / 1e9, TFLOPs=nf / (ms * 1e-3) / 1e12,
                rotated_sets=len(sets))
     res["hbm_frac"] = res["GBps"] / HBM_PEAK_GBS
@@ -129,6 +137,39 @@ def measure(wq, torch, index, M, steps, warmup, kernel="auto"):
     del sets, L
     torch.cuda.empty_cache()
     return res
+
+
+def stream_copy(torch, nbytes, steps=100):
+    """Context, not the denominator: torch's device-to-device copy of nbytes per
+    launch (nbytes read + nbytes written), rotating over >= 1 GiB of sources so
+    that reads come from HBM. Of torch's streaming kernels it is the fastest here,
+    so it shows what a generic library kernel reaches at this transfer size."""
+    n = nbytes // 4
+    R = max(1, min(64, math.ceil(ROTATE_BYTES / nbytes)))
+    bufs = [torch.ones(n, dtype=torch.int32, device="cuda") for _ in range(R)]
+    dst = torch.empty(n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(R):
+            dst.copy_(bufs[i])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            dst.copy_(bufs[i % R])
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / steps * 1e3
+    del g, bufs, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": n * 4, "bytes_written": n * 4, "us_per_launch": us,
+            "GBps_read_plus_write": 2 * n * 4 / (us * 1e-6) / 1e9}
 
 
 def measure_offline(wq, torch, index):
@@ -193,8 +234,13 @@ def cpu_baseline(budget_s=12.0):
     except Exception:  # pragma: no cover
         threads = 1
     W, x, cfg = workloads.make(2)
+    t0 = time.perf_counter()
     L = oracle.quantize_layer(W, 0)
+    t_quant = time.perf_counter() - t0
     N, K = W.shape
+    t0 = time.perf_counter()
+    oracle.dequant(L["q"], L["s"], L["z"])
+    t_deq = time.perf_counter() - t0
     times = []
     t_end = time.perf_counter() + budget_s
     while not times or time.perf_counter() < t_end:
@@ -203,9 +249,26 @@ def cpu_baseline(budget_s=12.0):
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     nb = alg_bytes(1, N, K, 0)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info() if i.get("user_api") == "blas"}))
+    except Exception:  # pragma: no cover
+        blas = "?"
     return {"value": nb / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"oracle linear_ref (fp64 dequantize + BLAS) on the full decode layer x[1,4096] "
-                      f"W[11008,4096], median of {len(times)} runs ({t * 1e3:.1f} ms each)"}
+                      f"W[11008,4096], median of {len(times)} runs ({t * 1e3:.1f} ms each)",
+            "host": {"cpu_count": os.cpu_count(), "model": model, "blas": blas},
+            "phases_ms": {"quantize_fp32": round(t_quant * 1e3, 1), "dequantize_fp64": round(t_deq * 1e3, 1),
+                          "linear_ref": round(t * 1e3, 1)}}
 
 
 def main():
@@ -250,19 +313,24 @@ def main():
             plan = []
             for item in args.workloads.split(","):
                 f = item.split(":")
-                plan.append((int(f[0]), int(f[1]), f[2] if len(f) > 2 else "auto"))
+                plan.append((int(f[0]), int(f[1]), f[2] if len(f) > 2 and f[2] else "auto",
+                             int(f[3]) if len(f) > 3 else None))
         else:
-            plan = [(3, 16, "auto"), (4, 2048, "auto"), (5, 1, "auto"), (5, 8, "auto"), (5, 64, "auto"),
-                    (5, 512, "auto")]
+            plan = [(3, 16, "auto", None), (4, 2048, "auto", None), (5, 1, "auto", None), (5, 8, "auto", None),
+                    (5, 64, "auto", None), (5, 512, "auto", None)]
             # the other kernel on either side of the crossover
             for M in (8, 64):
                 other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
-                plan.append((5, M, other))
-        for index, M, kern in plan:
+                plan.append((5, M, other, None))
+            # one GPU's shard of the 70B down-projection split over 8 GPUs along K
+            # (K / 8 = 3584 input channels, 28 groups)
+            plan += [(5, 1, "auto", 3584), (5, 512, "auto", 3584)]
+        for index, M, kern, Kov in plan:
             steps = max(20, min(args.steps, 100)) if M >= 64 else args.steps
-            r = measure(wq, torch, index, M, steps, min(args.warmup, 10), kernel=kern)
+            r = measure(wq, torch, index, M, steps, min(args.warmup, 10), kernel=kern, K=Kov)
             rows.append(r)
-            print(f"# {r['config']}:{r['M']} {r['kernel']:4s} {r['us_per_launch']:9.2f} us  "
+            print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov} {r['kernel']:4s} "
+                  f"{r['us_per_launch']:9.2f} us  "
                   f"{r['GBps']:8.1f} GB/s ({100 * r['hbm_frac']:5.1f}%)  {r['TFLOPs']:7.1f} TF/s "
                   f"({100 * r['mfma_frac']:5.1f}%)", file=sys.stderr, flush=True)
     if not args.quick and not args.no_offline:
@@ -271,6 +339,13 @@ def main():
             offline.append(o)
             print(f"# offline {o}", file=sys.stderr, flush=True)
 
+    context = None
+    if not args.quick:
+        context = {"torch_copy_headline_bytes": stream_copy(torch, alg_bytes(1, 11008, 4096, 0)),
+                   "torch_copy_256MiB": stream_copy(torch, 256 << 20, steps=20)}
+        print(f"# torch copy (context): {context['torch_copy_headline_bytes']['GBps_read_plus_write']:.1f} GB/s "
+              f"(read + write) at the headline size, "
+              f"{context['torch_copy_256MiB']['GBps_read_plus_write']:.1f} GB/s at 256 MiB", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline()
     us = head["us_per_launch"]
     line = {
@@ -289,10 +364,12 @@ def main():
         "config": {"workload": "decode GEMV, Llama-7B MLP up-proj: x fp16 [1,4096], W [11008,4096] "
                                "INT4 asym g128 packed 8/uint32, y fp16",
                    "M": 1, "N": 11008, "K": 4096, "group": 128, "kernel": head["kernel"],
-                   "rotated_sets": head["rotated_sets"]},
+                   "rotated_sets": head["rotated_sets"], "us_p10": round(head["us_p10"], 3),
+                   "us_p90": round(head["us_p90"], 3), "replays": head["replays"]},
         "roofline": {"bound": "hbm", "achieved": round(head["GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["hbm_frac"], 4), "traffic": recorded_traffic()},
         "cpu_baseline": cpu,
+        "context": context,
         "workloads": rows,
         "offline": offline,
     }
