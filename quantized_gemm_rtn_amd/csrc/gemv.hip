@@ -42,6 +42,8 @@
 // load under a divergent branch makes the compiler wait for all outstanding loads
 // where the branches join, which would serialize the stream. For the same reason
 // staged values are loaded before the weight prefetch is issued and stored after.
+#include <type_traits>
+
 #include "wq_device.h"
 #include "wq_launch.h"
 
@@ -53,6 +55,7 @@ constexpr int kGemvRingDepth = 4;  // D of gemv_ring_kernel
 constexpr int kNumCu = 256;
 constexpr int kGemvEarly = 8;   // weight groups issued before the wait on staged data
 constexpr int kXLdsMaxHalves = 32768;
+constexpr int kSparseBatch = 4;  // CSR entries per lane whose loads are in flight together
 // SZV value of gemv_lds_kernel for scales and zero-points held in registers (see below)
 constexpr int kSzInRegs = -1;
 // sched_barrier mask between consecutive groups of a window: scalar, MFMA, LDS and
@@ -68,23 +71,40 @@ constexpr int kSchedKeepGroups = 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x
 // read one group of 16 rows hit 16 different banks.
 //   SZV = 8, 4, 2: rows as vectors of SZV halves (G % SZV == 0, so no vector
 //     crosses a row; G <= kSzMaxG): <= 2, 2, 4 loads per thread
-//   SZV = 1: as halves (G <= 256): <= 16 loads per thread
+//   SZV = 1: as halves (G <= 64): <= 4 loads per thread
 //   SZV = 0: a plain loop (any G), run after the weight prefetch
 template <int V> struct SzBits;
 template <> struct SzBits<8> { typedef uint4 type; };
 template <> struct SzBits<4> { typedef uint2 type; };
 template <> struct SzBits<2> { typedef uint32_t type; };
 template <> struct SzBits<1> { typedef uint16_t type; };
-template <int V> struct Halves { f16 h[V]; };
+// the same bits as V halves, in a register type (indexing a bit-cast array would go
+// through scratch memory)
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+template <int V> struct SzHalves;
+template <> struct SzHalves<8> { typedef f16x8 type; };
+template <> struct SzHalves<4> { typedef f16x4 type; };
+template <> struct SzHalves<2> { typedef f16x2 type; };
+template <> struct SzHalves<1> { typedef f16 type; };
+template <int V>
+__device__ __forceinline__ f16 sz_half(const typename SzHalves<V>::type& v, int j) {
+  if constexpr (V == 1) {
+    return v;
+  } else {
+    return v[j];
+  }
+}
 // largest G each vector width is chosen for
-template <int V> constexpr int kSzMaxG = V == 8 || V == 1 ? 256 : 128;
+template <int V> constexpr int kSzMaxG = V == 8 ? 256 : (V == 1 ? 64 : 128);
 
 template <int SZV, int T>
 struct SzStage {
   static constexpr int V = SZV > 0 ? SZV : 1;
   static constexpr int C = SZV == 0 ? 0 : (16 * kSzMaxG<V> / V + T - 1) / T;
   typedef typename SzBits<V>::type Vec;
-  Vec vs[C > 0 ? C : 1], vz[C > 0 ? C : 1];
+  // single halves are held in 32-bit registers (arrays of 16-bit values stay in memory)
+  typedef typename std::conditional<V == 1, uint32_t, Vec>::type Reg;
+  Reg vs[C > 0 ? C : 1], vz[C > 0 ? C : 1];
 
   __device__ __forceinline__ void load(const f16* scales, const f16* zeros, int n0, int N, int G, int t) {
     const int nload = 16 * G / V;
@@ -107,10 +127,11 @@ struct SzStage {
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int idx = min(t + i * T, nload - 1);
-      const Halves<V> s = __builtin_bit_cast(Halves<V>, vs[i]), z = __builtin_bit_cast(Halves<V>, vz[i]);
+      typedef typename SzHalves<V>::type H;
+      const H s = __builtin_bit_cast(H, (Vec)vs[i]), z = __builtin_bit_cast(H, (Vec)vz[i]);
       const int base = V * idx + (V * idx) / G;  // row * (G + 1) + column
 #pragma unroll
-      for (int j = 0; j < V; ++j) sz[base + j] = f16x2{s.h[j], (f16)(k1024 + z.h[j])};
+      for (int j = 0; j < V; ++j) sz[base + j] = f16x2{sz_half<V>(s, j), (f16)(k1024 + sz_half<V>(z, j))};
     }
     if constexpr (SZV == 0) {
       for (int idx = t; idx < 16 * G; idx += T) {
@@ -119,6 +140,29 @@ struct SzStage {
         sz[idx + row] = f16x2{scales[o], (f16)(k1024 + zeros[o])};
       }
     }
+  }
+};
+
+// The first B CSR entries of a lane's share of a row (entries e0, e0 + KW, ... below
+// e1), loaded in the prologue so that their latency hides under the weight stream.
+// Loads are unconditional: indices are clamped into the row, or to entry 0 for an
+// empty row (the product only takes this path with nnz >= 1), and values stay raw
+// fp16 until use, since converting them would wait for the load on the spot.
+template <int B, int KW>
+struct SparseHead {
+  int c[B];
+  f16 v[B];
+  __device__ __forceinline__ void load(const int32_t* col, const f16* val, int e0, int e1) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int eb = max(min(e0 + b * KW, e1 - 1), 0);
+      c[b] = col[eb];
+      v[b] = val[eb];
+    }
+  }
+  // value of entry b, 0 past the row end
+  __device__ __forceinline__ float weight(int b, int e0, int e1) const {
+    return e0 + b * KW < e1 ? (float)v[b] : 0.0f;
   }
 };
 
@@ -226,7 +270,7 @@ __device__ __forceinline__ void reduce_store(f32x4 acc, int wave, int lane, int 
 }
 
 // ---------------------------------------------------------------------------
-template <int KW, int D, int XC, int SZV, int MR>
+template <int KW, int D, int XC, int SZV, int MR, bool SP>
 __global__ void __launch_bounds__(64 * KW)
 gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
                 const f16* __restrict__ scales, const f16* __restrict__ zeros, int N,
@@ -258,6 +302,12 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   const int ng = g_hi - g_lo;
 
   // ---- prologue: staging loads, weight prefetch, staging stores
+  // CSR bounds of the lane's row go out first: the wait on the staging loads covers them
+  int sp_e0 = 0, sp_e1 = 0;
+  if constexpr (SP) {
+    sp_e0 = row_ptr[n_ld] + wave;
+    sp_e1 = row_ptr[n_ld + 1];
+  }
   SzStage<SZV == kSzInRegs ? 8 : SZV, T> szs;
   if constexpr (SZV != kSzInRegs) szs.load(scales, zeros, n0, N, G, t);
   // the block's rows of x are contiguous in memory and in LDS
@@ -327,6 +377,8 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = D0; i < D; ++i) prefetch(i);
+  SparseHead<kSparseBatch, KW> sph;
+  if constexpr (SP) sph.load(col, val, sp_e0, sp_e1);
   __syncthreads();
 
   // ---- main loop over this wave's groups
@@ -414,18 +466,24 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   // ---- sparse outlier term for column n = n0 + r (entries split over the KW
   // waves), activations from LDS
   const int n = n0 + r;
-  if (row_ptr != nullptr && n < N) {
-    const int e1 = row_ptr[n + 1];
-    for (int e = row_ptr[n] + wave; e < e1; e += KW) {
-      const int c = col[e];
-      const float v = (float)val[e];
+  if constexpr (SP) {
+    const auto add = [&](int c, float v) {
       const int cs = (c & ~7) | perm_slot(c & 7);
-      const float unscale = (c & 1) ? 16.0f : 1.0f;  // odd channels were stored / 16
+      const float vu = (c & 1) ? 16.0f * v : v;  // odd channels were stored / 16
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = min(4 * h + i, mrows - 1);
-        acc[i] += v * ((float)xs[(size_t)m * K + cs] * unscale);
+        acc[i] += vu * (float)xs[(size_t)m * K + cs];
       }
+    };
+#pragma unroll
+    for (int b = 0; b < kSparseBatch; ++b) add(sph.c[b], sph.weight(b, sp_e0, sp_e1));
+    // the rest of the row, kSparseBatch entries per pass
+    for (int e = sp_e0 + kSparseBatch * KW; e < sp_e1; e += kSparseBatch * KW) {
+      SparseHead<kSparseBatch, KW> more;
+      more.load(col, val, e, sp_e1);
+#pragma unroll
+      for (int b = 0; b < kSparseBatch; ++b) add(more.c[b], more.weight(b, e, sp_e1));
     }
   }
   reduce_store<KW>(acc, wave, lane, m0, mrows, n, N, y, y_f32);
@@ -439,7 +497,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
 // Rows of the slot are 272 bytes apart, so the 16 rows of a fragment read fall in
 // distinct banks. One wave writes and reads its slot, and LDS instructions of a
 // wave execute in order, so no barrier is involved.
-template <int KW, int D, int XL, int NT, int SZV>
+template <int KW, int D, int XL, int NT, int SZV, bool SP>
 __global__ void __launch_bounds__(64 * KW)
 gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
                  const f16* __restrict__ scales, const f16* __restrict__ zeros, int N,
@@ -471,6 +529,18 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
 #pragma unroll
   for (int j = 0; j < XL; ++j) xst[j] = x + (size_t)(m0 + min(h + 4 * j, mrows - 1)) * K + 8 * r;
 
+  // CSR bounds of the lane's rows go out first: the wait on the staging loads covers
+  // them (ragged N: a valid row is walked and never stored)
+  int sp_e0[NT], sp_e1[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    sp_e0[j] = sp_e1[j] = 0;
+    if constexpr (SP) {
+      const int nr = min(n0 + 16 * j + r, N - 1);
+      sp_e0[j] = row_ptr[nr] + wave;
+      sp_e1[j] = row_ptr[nr + 1];
+    }
+  }
   SzStage<SZV, T> szs[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) szs[j].load(scales, zeros, min(n0 + 16 * j, N - 1), N, G, t);
@@ -488,6 +558,13 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
 #pragma unroll
   for (int j = 0; j < NT; ++j) szs[j].store(sz + j * 16 * (G + 1), scales, zeros, min(n0 + 16 * j, N - 1), N, G, t);
   __syncthreads();
+  // the first CSR entries of each row, behind the initial weight prefetch
+  constexpr int HB = kSparseBatch / NT;
+  SparseHead<HB, KW> sph[NT];
+  if constexpr (SP) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) sph[j].load(col, val, sp_e0[j], sp_e1[j]);
+  }
 
   const f16x2* szr = sz + r * (G + 1);
   const uint32_t magic = magic_1024x2();
@@ -534,6 +611,17 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
     }
     gs = gs_next;
   }
+  // activations of the first CSR entries, gathered before the last window so that
+  // its groups cover their latency
+  f16 spx[NT][HB][4];
+  if constexpr (SP) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int b = 0; b < HB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) spx[j][b][i] = x[(size_t)(m0 + min(4 * h + i, mrows - 1)) * K + sph[j].c[b]];
+  }
   if (win.last_lo == 0 && win.last_hi == D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) group(wbuf[i], xbuf[i], g_lo + gs + i);
@@ -543,19 +631,29 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
       if (i >= win.last_lo && i < win.last_hi) group(wbuf[i], xbuf[i], g_lo + gs + i);
   }
 
-  if (row_ptr != nullptr) {
+  if constexpr (SP) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int n = n0 + 16 * j + r;
-      if (n >= N) continue;
-      const int e1 = row_ptr[n + 1];
-      for (int e = row_ptr[n] + wave; e < e1; e += KW) {
-        const int c = col[e];
-        const float v = (float)val[e];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = min(4 * h + i, mrows - 1);
-          acc[j][i] += v * (float)x[(size_t)(m0 + m) * K + c];
+      for (int b = 0; b < HB; ++b) {
+        const float v = sph[j].weight(b, sp_e0[j], sp_e1[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] += v * (float)spx[j][b][i];
+      }
+      // the rest of the row, kSparseBatch entries per pass, their loads in flight together
+      for (int e = sp_e0[j] + HB * KW; e < sp_e1[j]; e += kSparseBatch * KW) {
+        SparseHead<kSparseBatch, KW> more;
+        more.load(col, val, e, sp_e1[j]);
+        f16 xv[kSparseBatch][4];
+#pragma unroll
+        for (int b = 0; b < kSparseBatch; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xv[b][i] = x[(size_t)(m0 + min(4 * h + i, mrows - 1)) * K + more.c[b]];
+#pragma unroll
+        for (int b = 0; b < kSparseBatch; ++b) {
+          const float v = more.weight(b, e, sp_e1[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][i] += v * (float)xv[b][i];
         }
       }
     }
@@ -590,7 +688,7 @@ static hipError_t launch_rows(Kern kern, size_t lds, int cols, const uint16_t* x
   return hipSuccess;
 }
 
-template <int XC, int SZV, int MR>
+template <int XC, int SZV, int MR, bool SP>
 static hipError_t launch_lds(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                              const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
@@ -598,17 +696,17 @@ static hipError_t launch_lds(const uint16_t* x, int64_t M, int64_t K, const uint
   const int64_t G = K / kGroup, mrows = M < 16 ? M : 16, SR = MR == 1 ? 1 : 4 * ((mrows + 3) / 4);
   const size_t lds = (SZV == kSzInRegs ? 0 : (size_t)16 * (G + 1) * 4) + (size_t)mrows * K * 2 +
                      (size_t)2 * G * SR * 4;
-  return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR>, lds, 16, x, M, K, packed, scales, zeros, N,
+  return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR, SP>, lds, 16, x, M, K, packed, scales, zeros, N,
                      row_ptr, col, val, y, y_f32, stream, &lds_set);
 }
 
-template <int XL, int NT, int SZV>
+template <int XL, int NT, int SZV, bool SP>
 static hipError_t launch_ring(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                               const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                               const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
   static size_t lds_set = 0;
   const size_t lds = (size_t)NT * 16 * (K / kGroup + 1) * 4 + (size_t)kGemvWaves * 4 * XL * 136 * 2;
-  return launch_rows(gemv_ring_kernel<kGemvWaves, kGemvRingDepth, XL, NT, SZV>, lds, 16 * NT, x, M, K, packed,
+  return launch_rows(gemv_ring_kernel<kGemvWaves, kGemvRingDepth, XL, NT, SZV, SP>, lds, 16 * NT, x, M, K, packed,
                      scales, zeros, N, row_ptr, col, val, y, y_f32, stream, &lds_set);
 }
 
@@ -616,6 +714,8 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
   const int64_t G = K / kGroup;
+  // a CSR is passed only with nnz >= 1: its kernels may read entry 0 of an empty row
+  const bool sp = row_ptr != nullptr;
   const int64_t mrows_max = M < 16 ? M : 16;
   // scales/zeros rows as vectors of 8, 4 or 2 halves when G is a multiple of the
   // width and every row starts aligned to it
@@ -642,8 +742,11 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   const int xc = mrows_max * K > kXLdsMaxHalves || mrows_max > 2 ? 0
                  : xloads <= 1 ? 1 : xloads <= 2 ? 2 : xloads <= 4 ? 4 : xloads <= 8 ? 8 : 16;
 #define WQ_ARGS x, M, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, stream
-#define WQ_LDS(XC, SV, MR) \
-  if (xc == XC && sz_mode == SV && mr == MR) return launch_lds<XC, SV, MR>(WQ_ARGS)
+#define WQ_LDS(XC, SV, MR)                                 \
+  if (xc == XC && sz_mode == SV && mr == MR) {             \
+    if (sp) return launch_lds<XC, SV, MR, true>(WQ_ARGS);  \
+    return launch_lds<XC, SV, MR, false>(WQ_ARGS);         \
+  }
 #define WQ_LDS_MR(XC, SV) WQ_LDS(XC, SV, 1); WQ_LDS(XC, SV, 2)
   WQ_LDS_MR(1, kSzInRegs); WQ_LDS_MR(2, kSzInRegs); WQ_LDS_MR(4, kSzInRegs); WQ_LDS_MR(8, kSzInRegs);
   WQ_LDS_MR(16, kSzInRegs);
@@ -657,13 +760,16 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   // two 16-channel tiles per wave share each staged activation fragment, as long as
   // the grid still has a block for every CU
   const int nt = ((N + 31) / 32) * ((M + 15) / 16) >= kNumCu ? 2 : 1;
-#define WQ_RING(XL, NT) \
-  if (xl == XL && nt == NT) { \
-    if (sv == 8) return launch_ring<XL, NT, 8>(WQ_ARGS); \
-    if (sv == 4) return launch_ring<XL, NT, 4>(WQ_ARGS); \
-    if (sv == 2) return launch_ring<XL, NT, 2>(WQ_ARGS); \
-    if (sv == 1) return launch_ring<XL, NT, 1>(WQ_ARGS); \
-    return launch_ring<XL, NT, 0>(WQ_ARGS); \
+#define WQ_RING_SV(XL, NT, SP)                                   \
+  if (sv == 8) return launch_ring<XL, NT, 8, SP>(WQ_ARGS);       \
+  if (sv == 4) return launch_ring<XL, NT, 4, SP>(WQ_ARGS);       \
+  if (sv == 2) return launch_ring<XL, NT, 2, SP>(WQ_ARGS);       \
+  if (sv == 1) return launch_ring<XL, NT, 1, SP>(WQ_ARGS);       \
+  return launch_ring<XL, NT, 0, SP>(WQ_ARGS);
+#define WQ_RING(XL, NT)            \
+  if (xl == XL && nt == NT) {      \
+    if (sp) { WQ_RING_SV(XL, NT, true) } \
+    WQ_RING_SV(XL, NT, false)      \
   }
   WQ_RING(1, 1);
   WQ_RING(2, 1);
@@ -672,6 +778,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   WQ_RING(2, 2);
   WQ_RING(4, 2);
 #undef WQ_RING
+#undef WQ_RING_SV
   return hipErrorInvalidValue;  // not reached
 #undef WQ_LDS
 #undef WQ_ARGS
