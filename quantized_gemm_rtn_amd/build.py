@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -32,6 +33,10 @@ COMMON = [
 ]
 # The quantizer and split decide integers with float32 arithmetic: no contraction.
 PER_FILE = {"quant.hip": ["-ffp-contract=off"], "split.hip": ["-ffp-contract=off"]}
+# The product kernels must keep everything in registers and LDS: the compiler
+# reports each kernel's per-lane scratch, and any use of it fails the build.
+NO_SCRATCH = {"gemv.hip", "gemm.hip"}
+RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
 
 
 def hipcc() -> str:
@@ -43,15 +48,35 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [hipcc(), *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    check = src in NO_SCRATCH
+    cmd = [hipcc(), *COMMON, *PER_FILE.get(src, []), *([RESOURCE_REMARK] if check else []),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    if verbose and r.stderr.strip():
+    if check:
+        bad = scratch_users(r.stderr)
+        if bad:
+            raise RuntimeError(f"{src}: kernels using scratch memory (bytes per lane): {bad}")
+    elif verbose and r.stderr.strip():
         print(r.stderr, file=sys.stderr)
     return obj
+
+
+def scratch_users(remarks: str) -> dict:
+    """Kernels with a nonzero ScratchSize in the compiler's resource-usage remarks."""
+    bad, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            bad[name] = int(m.group(1))
+    return bad
 
 
 def build(verbose: bool = False) -> str:
