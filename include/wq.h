@@ -25,7 +25,9 @@
  *  - Preconditions the device does not check: inputs are finite; a group's
  *    range (max - min) is at most 15 * 65504 and every |w| of a sparse entry at
  *    most 65504, so scales and sparse values fit fp16; INT4 codes are <= 15.
- *  - Integer sizes: 1 <= N, 1 <= M, K a positive multiple of 128, N*K < 2^31.
+ *  - Integer sizes: 1 <= N, 0 <= M, K a positive multiple of 128, N*K < 2^31.
+ *    M = 0 (an empty batch) returns WQ_OK without launching anything; x and y
+ *    may then be NULL.
  *  - Alignment: W, x, codes and packed must be 16-byte aligned (WQ_ERR_ALIGN).
  */
 #ifndef WQ_H

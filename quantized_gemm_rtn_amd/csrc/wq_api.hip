@@ -21,13 +21,15 @@ int check_linear_args(const uint16_t* x, int64_t M, int64_t K, const uint32_t* p
                       const uint16_t* zeros, int64_t N, int32_t group, const int32_t* row_ptr,
                       const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int32_t y_dtype,
                       int32_t kernel) {
-  if (!x || !packed || !scales || !zeros || !y) return WQ_ERR_NULL;
+  // M = 0 (an empty batch) is valid and computes nothing; x and y may then be NULL
+  if (!packed || !scales || !zeros) return WQ_ERR_NULL;
+  if (M != 0 && (!x || !y)) return WQ_ERR_NULL;
   if (row_ptr == nullptr && nnz != 0) return WQ_ERR_NULL;
   if (nnz > 0 && (!col || !val)) return WQ_ERR_NULL;
   if (group != kGroup) return WQ_ERR_UNSUPPORTED;
   if (y_dtype != WQ_F16 && y_dtype != WQ_F32) return WQ_ERR_UNSUPPORTED;
   if (kernel != WQ_KERNEL_AUTO && kernel != WQ_KERNEL_GEMV && kernel != WQ_KERNEL_GEMM) return WQ_ERR_UNSUPPORTED;
-  if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) return WQ_ERR_SHAPE;
+  if (M < 0 || N < 1 || K < kGroup || K % kGroup != 0) return WQ_ERR_SHAPE;
   if (nnz < 0 || nnz >= kMax32) return WQ_ERR_SHAPE;
   if (N >= kMax32 / K || M >= kMax32 / K || M >= kMax32 / N) return WQ_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(zeros, 2) || !aligned(y, 4))
@@ -116,6 +118,7 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K, const uint3
   const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
                                    kernel);
   if (rc != WQ_OK) return rc;
+  if (M == 0) return WQ_OK;
   if (kernel == WQ_KERNEL_AUTO) kernel = wq_auto_kernel(M, N, K);
   const int y_f32 = y_dtype == WQ_F32;
   const int32_t* rp = nnz > 0 ? row_ptr : nullptr;  // nnz == 0: the dense product

@@ -85,13 +85,23 @@ def linear(lib, x=A, M=1, K=256, packed=A2, scales=A3, zeros=A4, N=64, group=128
     (dict(y=None), -1), (dict(nnz=5, row_ptr=None), -1), (dict(row_ptr=A, nnz=3, col=None, val=A2), -1),
     (dict(row_ptr=A, nnz=3, col=A2, val=None), -1),
     (dict(group=64), -4), (dict(y_dtype=2), -4), (dict(kernel=3), -4),
-    (dict(M=0), -2), (dict(N=0), -2), (dict(K=0), -2), (dict(K=100), -2), (dict(K=64), -2),
+    (dict(M=-1), -2), (dict(N=0), -2), (dict(K=0), -2), (dict(K=100), -2), (dict(K=64), -2),
     (dict(nnz=-1, row_ptr=A), -2), (dict(M=1 << 20, K=4096), -2), (dict(N=1 << 20, K=4096), -2),
     (dict(x=MIS), -3), (dict(packed=MIS), -3), (dict(scales=ctypes.c_void_p(0x7F0000000001)), -3),
     (dict(y=ctypes.c_void_p(0x7F0000000002)), -3),
 ])
 def test_linear_validation(lib, kw, status):
     assert linear(lib, **kw) == status
+
+
+def test_empty_batch_is_a_no_op(lib):
+    """M = 0 computes nothing and accepts NULL activations and output, but the
+    weights and the other sizes are still checked (no HIP call either way)."""
+    assert linear(lib, M=0, x=None, y=None) == 0
+    assert linear(lib, M=0, x=None, y=None, kernel=2) == 0
+    assert linear(lib, M=0, x=None, y=None, packed=None) == -1
+    assert linear(lib, M=0, x=None, y=None, K=100) == -2
+    assert linear(lib, M=1, x=None) == -1
 
 
 def test_linear_wrappers_validate(lib):

@@ -67,6 +67,17 @@ def test_config5_sweep_sampled(gpu_lib, M):
     _sampled_check(gpu_lib, torch, L, x, "auto", sample_rows(L["q"].shape[0], 96, 5 + M), f"config 5")
 
 
+@pytest.mark.parametrize("M", [1, 512])
+def test_config5_shard_sampled(gpu_lib, M):
+    """One GPU's share of the 70B down-projection split eight ways along K
+    (x [M, 3584], W [8192, 3584] with its share of the CSR), in the launch
+    configuration the benchmark times."""
+    import torch
+    L = oracle_layer(5, K=3584)
+    _, x, _ = workloads.make(5, M=M, K=3584)
+    _sampled_check(gpu_lib, torch, L, x, "auto", sample_rows(L["q"].shape[0], 96, 50 + M), "config 5 shard")
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 7, 15, 16, 17, 31, 33, 64, 65, 130])
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
 def test_ragged_shapes(gpu_lib, M, kernel):
@@ -222,3 +233,15 @@ def test_end_to_end_gpu_pipeline(gpu_lib):
                               out["val"])
     ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
     assert oracle.rel_err_inf(y.float().cpu().numpy(), ref) <= TOL
+
+
+def test_empty_batch(gpu_lib):
+    """M = 0 through the binding: an empty [0, N] result, with and without a CSR."""
+    import torch
+    L = oracle_layer(1)
+    D = layer_to_dev(L, torch)
+    x = torch.empty((0, L["q"].shape[1]), dtype=torch.float16, device="cuda")
+    for sparse in (False, True):
+        y = run_linear(gpu_lib, x, D, sparse=sparse)
+        torch.cuda.synchronize()
+        assert tuple(y.shape) == (0, L["q"].shape[0])
