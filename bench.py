@@ -1,20 +1,21 @@
 """Benchmark of the W4A16 group-quantized linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--quick]
+    python bench.py [--gpus 1] [--steps 3000] [--warmup 20] [--quick]
 
 A step is one call of the online hot path, wq_linear_sparse (kernel chosen by
 M, sparse term fused), on the headline workload: the decode GEMV of a Llama-7B
-MLP up-projection, x fp16 [1, 4096], W [11008, 4096] INT4 g128 (the second
-workload of the task's configuration list).  The weights are quantized and
+MLP up-projection, x fp16 [1, 4096], W [11008, 4096] INT4 g128.  The weights are quantized and
 packed on the GPU by wq_quantize_rtn / wq_pack before timing (offline steps,
 reported separately under "offline").
 
 Inputs stay resident in HBM: R copies of the layer (packed codes, scales,
 zeros, CSR, x, y) totalling >= 1 GiB are rotated so no launch is served from
-the 256 MB Infinity Cache.  The K timed launches are captured in one HIP graph
-and replayed five times, each between synchronizations; HIP events on the
-launch stream bracket each replay, and the median replay gives the figures
-(p10 and p90 are reported beside them).
+the 256 MB Infinity Cache.  After W warm-up launches, the K timed launches are
+captured in one HIP graph and replayed five times, each between
+synchronizations; HIP events on the launch stream bracket each replay, and the
+median replay gives the figures (p10 and p90 are reported beside them).  The
+default K spans about 20 ms per replay; the other workloads size their replays
+the same way (at least 200 launches and 20 ms, from one timed replay of 20).
 
 Printed: ONE JSON line with the metric (GB/s, algorithmic bytes), the roofline
 of the dominant kernel, the CPU oracle baseline, and the other workloads
@@ -119,15 +120,26 @@ def time_launches(wq, torch, sets, steps, warmup, kernel="auto", repeats=5):
     return per_launch
 
 
+def replay_length(wq, torch, sets, kernel, min_ms=25.0, min_steps=200, max_steps=20000):
+    """Launches per replay so that one replay spans at least min_steps and about
+    min_ms (25 ms, so that the 20 ms floor holds when the estimate from one timed
+    replay of 20 captured launches runs high)."""
+    t = time_launches(wq, torch, sets, 20, 0, kernel, repeats=1)[0]
+    return int(min(max_steps, max(min_steps, math.ceil(min_ms / t))))
+
+
 def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None):
+    """steps = None: enough launches per replay for >= 20 ms (and >= 200 launches)."""
     L = Layer(wq, torch, index, M, K)
     sets = L.sets(torch, ROTATE_BYTES)
+    if steps is None:
+        steps = replay_length(wq, torch, sets, kernel)
     runs = time_launches(wq, torch, sets, steps, warmup, kernel)
     ms = float(np.median(runs))
     nb = alg_bytes(M, L.N, L.K, L.sparse_k)
     nf = alg_flops(M, L.N, L.K, L.sparse_k)
     used = kernel if kernel != "auto" else wq.auto_kernel(M, L.N, L.K)
-    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, kernel=used, us_per_launch=ms * 1e3,
+    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, kernel=used, steps=steps, us_per_launch=ms * 1e3,
                us_p10=float(np.percentile(runs, 10)) * 1e3, us_p90=float(np.percentile(runs, 90)) * 1e3,
                replays=len(runs),
                alg_bytes=nb, alg_flops=nf, GBps=nb / (ms * 1e-3) / 1e9, TFLOPs=nf / (ms * 1e-3) / 1e12,
@@ -274,7 +286,8 @@ def cpu_baseline(budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=3000,
+                    help="launches per timed replay of the headline workload (the default spans about 20 ms)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -326,8 +339,7 @@ def main():
             # (K / 8 = 3584 input channels, 28 groups)
             plan += [(5, 1, "auto", 3584), (5, 512, "auto", 3584)]
         for index, M, kern, Kov in plan:
-            steps = max(20, min(args.steps, 100)) if M >= 64 else args.steps
-            r = measure(wq, torch, index, M, steps, min(args.warmup, 10), kernel=kern, K=Kov)
+            r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov)
             rows.append(r)
             print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov} {r['kernel']:4s} "
                   f"{r['us_per_launch']:9.2f} us  "
