@@ -128,13 +128,13 @@ def replay_length(wq, torch, sets, kernel, min_ms=25.0, min_steps=200, max_steps
     return int(min(max_steps, max(min_steps, math.ceil(min_ms / t))))
 
 
-def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None):
+def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5):
     """steps = None: enough launches per replay for >= 20 ms (and >= 200 launches)."""
     L = Layer(wq, torch, index, M, K)
     sets = L.sets(torch, ROTATE_BYTES)
     if steps is None:
         steps = replay_length(wq, torch, sets, kernel)
-    runs = time_launches(wq, torch, sets, steps, warmup, kernel)
+    runs = time_launches(wq, torch, sets, steps, warmup, kernel, repeats=replays)
     ms = float(np.median(runs))
     nb = alg_bytes(M, L.N, L.K, L.sparse_k)
     nf = alg_flops(M, L.N, L.K, L.sparse_k)
@@ -290,6 +290,7 @@ def main():
                     help="launches per timed replay of the headline workload (the default spans about 20 ms)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--replays", type=int, default=5, help="timed replays per workload (median, p10, p90)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel],... "
                     "(default: the batched-decode, prefill and 70B-sweep set)")
@@ -316,7 +317,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head = measure(wq, torch, 2, 1, args.steps, args.warmup)
+    head = measure(wq, torch, 2, 1, args.steps, args.warmup, replays=args.replays)
     print(f"# headline 2:1 {head['kernel']} {head['us_per_launch']:.2f} us  {head['GBps']:.1f} GB/s "
           f"({100 * head['hbm_frac']:.1f}% of HBM peak)", file=sys.stderr, flush=True)
     rows = []
@@ -339,7 +340,7 @@ def main():
             # (K / 8 = 3584 input channels, 28 groups)
             plan += [(5, 1, "auto", 3584), (5, 512, "auto", 3584)]
         for index, M, kern, Kov in plan:
-            r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov)
+            r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov, replays=args.replays)
             rows.append(r)
             print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov} {r['kernel']:4s} "
                   f"{r['us_per_launch']:9.2f} us  "
