@@ -245,3 +245,40 @@ def test_empty_batch(gpu_lib):
         y = run_linear(gpu_lib, x, D, sparse=sparse)
         torch.cuda.synchronize()
         assert tuple(y.shape) == (0, L["q"].shape[0])
+
+
+def test_sparse_split_under_graph_capture(gpu_lib):
+    """A CSR product whose GEMM splits K (transpose, split GEMM, slice sum with the
+    sparse term) captured in a CUDA graph: every replay equals the eager result,
+    with eager calls and synchronizations between the replays."""
+    import torch
+    M, N, K = 200, 256, 4096
+    W = workloads.random_weights(77, N, K)
+    L = oracle.quantize_layer(W, N * K // 200)
+    x = workloads.random_x(78, M, K)
+    D = layer_to_dev(L, torch)
+    xd = to_dev(x, torch)
+    ws = torch.empty(gpu_lib.linear_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+
+    def call(out=None):
+        return gpu_lib.linear_sparse(xd, D["packed"], D["scales"], D["zeros"], D["row_ptr"], D["col"], D["val"],
+                                     out=out, workspace=ws)
+
+    eager = call()
+    torch.cuda.synchronize()
+    ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    assert oracle.rel_err_inf(eager.float().cpu().numpy(), ref) <= TOL
+    out = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        call(out)
+    for i in range(4):
+        say(f"[graph] replay {i}")
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+        again = call()
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager), i
