@@ -312,7 +312,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
 }
 
 constexpr int kBigSS = 128;                // halves per super-step (one group)
-constexpr int kBigStride = kBigSS + 8;     // halves per padded LDS row: 68 dwords, 4 mod 32
 constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 groups x 256 columns
 
 // Dense kernel for large M. As launched: block tile 128 x 256, four waves side by
@@ -604,210 +603,6 @@ gemm_big_kernel(GemmArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Dense kernel for 16 < M <= 64: block tile 64 x 256, four waves of 64 x 64 (2 x 2
-// subtiles of 32 x 32), two blocks per compute unit, K split across blocks. At this M
-// the product streams the weights, and a super-step of one group is only 32 MFMAs per
-// wave, so the weights are loaded three super-steps ahead into a ring of four
-// register sets, and the activations two super-steps ahead (through two register
-// sets and two LDS stages). The loop body is four super-steps, so every ring index
-// is a constant (slices are multiples of four groups).
-template <int MINB>
-__global__ void __launch_bounds__(256, MINB)
-gemm_skinny_kernel(GemmArgs a) {
-  constexpr int BM = 64, BN = 256, WTN = 64, MT = 2, NT = 2;
-  constexpr int STAGE = BM * kBigStride;
-
-  extern __shared__ __align__(16) f16 smem[];
-  uint32_t* szl = reinterpret_cast<uint32_t*>(smem + 2 * STAGE);
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wn = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int h = lane >> 5, c32 = lane & 31;
-  const int M = a.M, N = a.N, K = a.K;
-  const int G = K >> 7;  // a multiple of 4
-
-  const int ntile = a.tiles_m * a.tiles_n;
-  const int nblk = ntile * a.ksplit;
-  int bid = blockIdx.x;
-  if (nblk % kNumXcd == 0) bid = (bid % kNumXcd) * (nblk / kNumXcd) + bid / kNumXcd;
-  const int slice = bid / ntile;
-  const int tile = bid - slice * ntile;
-  const int m0 = (tile % a.tiles_m) * BM, n0 = (tile / a.tiles_m) * BN;
-  const int g0 = slice * (a.k_per_slice >> 7);                  // a multiple of 4
-  const int ng = min(G, g0 + (a.k_per_slice >> 7)) - g0;        // a multiple of 4
-
-  // activations: thread t loads row (t >> 4) + 16 i (i < 4), 16-byte chunk t & 15
-  const int xch = t & 15, xrow0 = m0 + (t >> 4);
-  const int xdst0 = (t >> 4) * kBigStride + 8 * xch;
-  uint32_t woff[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const uint32_t n = (uint32_t)min(n0 + wn * WTN + 32 * j + c32, N - 1);
-    woff[j] = n * (uint32_t)(K >> 3) + 4 * h;
-  }
-  const uint32_t szoff = (uint32_t)min(n0 + t, N - 1) * (uint32_t)G + (uint32_t)g0;
-
-  uint4 w0[NT][2], w1[NT][2], w2[NT][2], w3[NT][2];  // weight ring
-  uint4 xa[4], xb[4];                                // activation register sets
-  uint32_t sp = 0, zp = 0;
-  auto wset = [&](int r) -> uint4(&)[NT][2] { return r == 0 ? w0 : r == 1 ? w1 : r == 2 ? w2 : w3; };
-  auto load_w_part = [&](uint4 (&W)[NT][2], int g, int j) {
-    const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
-    const uint32_t o = woff[j] + 16 * gg;
-    W[j][0] = *reinterpret_cast<const uint4*>(a.packed + o);
-    W[j][1] = *reinterpret_cast<const uint4*>(a.packed + o + 8);
-  };
-  auto load_x_part = [&](uint4 (&X)[4], int g, int i) {
-    const uint32_t gg = (uint32_t)(g0 + min(g, ng - 1));
-    const uint32_t row = (uint32_t)min(xrow0 + 16 * i, M - 1);
-    X[i] = *reinterpret_cast<const uint4*>(a.x + (row * (uint32_t)K + 128 * gg + 8 * xch));
-  };
-  auto store_x_part = [&](const uint4 (&X)[4], f16* st, int i) {
-    *reinterpret_cast<uint4*>(st + xdst0 + 16 * i * kBigStride) = perm_x8(X[i]);
-  };
-  auto load_sz = [&](int g) {
-    const uint32_t o = szoff + (uint32_t)min(g, ng - 2);
-    sp = *reinterpret_cast<const uint32_t*>(a.scales + o);
-    zp = *reinterpret_cast<const uint32_t*>(a.zeros + o);
-  };
-  auto store_sz = [&](int buf) {
-    szl[(2 * buf) * 256 + t] = (sp & 0xFFFFu) | (zp << 16);
-    szl[(2 * buf + 1) * 256 + t] = (sp >> 16) | (zp & 0xFFFF0000u);
-  };
-  auto read_sz = [&](uint32_t (&sz)[NT], int buf, int grp) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) sz[j] = szl[(2 * buf + grp) * 256 + wn * WTN + 32 * j + c32];
-  };
-  const uint32_t magic = magic_1024x2();
-  auto read_a = [&](f16x8 (&av)[MT], const f16* xs, int ks) {
-    const int kk = 64 * (ks >> 2) + 32 * h + 8 * (ks & 3);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) av[i] = *reinterpret_cast<const f16x8*>(xs + (32 * i + c32) * kBigStride + kk);
-  };
-  auto deq_b = [&](const uint4 (&W)[NT][2], int j, int ks, uint32_t sz) {
-    const f16x2 sz2 = as_f16x2(sz);
-    const f16 zb = (f16)1024.0f + sz2[1], zn = -((f16)64.0f + sz2[1]);
-    const f16x2 bias = {zb, zb}, nbias16 = {zn, zn}, s2 = {sz2[0], sz2[0]};
-    const uint4& q = W[j][ks >> 2];
-    const int c = ks & 3;
-    const uint32_t w = c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
-    return as_f16x8(dequant_word_x16(w, magic, bias, nbias16, s2));
-  };
-
-  f32x16 acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  f16x8 a0[MT], a1[MT];
-  f16x8 bcur;
-  uint32_t szc[NT], szn[NT];
-  // super-step g = 4 it + i: weights of set i, activations from stage i % 2; loads the
-  // weights of g + 3 into set (i + 3) % 4 and the activations of g + 2 into register
-  // set i % 2, and stores those of g + 1 (register set (i + 1) % 2) to stage (i + 1) % 2
-  auto superstep = [&](int g, int i) {
-    const uint4(&W)[NT][2] = wset(i);
-    uint4(&Wl)[NT][2] = wset((i + 3) & 3);
-    uint4(&Xl)[4] = (i & 1) ? xb : xa;
-    const uint4(&Xs)[4] = (i & 1) ? xa : xb;
-    const f16* xs = smem + (i & 1) * STAGE;
-    f16* xn = smem + ((i + 1) & 1) * STAGE;
-    const int pp = i & 1, buf = (i >> 1) & 1;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      f16x8(&cur)[MT] = (ks & 1) ? a1 : a0;
-      f16x8(&nxt)[MT] = (ks & 1) ? a0 : a1;
-      if (ks < 4) load_x_part(Xl, g + 2, ks);
-      if (ks < NT) load_w_part(Wl, g + 3, ks);
-      if (ks >= 4) store_x_part(Xs, xn, ks - 4);
-      if (ks == 0 && pp == 1) load_sz(g + 3);
-      if (ks == 4 && pp == 0) store_sz(buf ^ 1);
-      if (ks == 6) read_sz(szn, pp == 0 ? buf : buf ^ 1, pp ^ 1);
-      if (ks < 7) read_a(nxt, xs, ks + 1);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const f16x8 bnext = j + 1 < NT ? deq_b(W, j + 1, ks, szc[j + 1])
-                                       : (ks < 7 ? deq_b(W, 0, ks + 1, szc[0])
-                                                 : deq_b(wset((i + 1) & 3), 0, 0, szn[0]));
-#pragma unroll
-        for (int r = 0; r < MT; ++r) acc[r][j] = mfma_32x32x16(cur[r], bcur, acc[r][j]);
-        bcur = bnext;
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (ks < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-        else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    read_a(a0, xn, 0);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) szc[j] = szn[j];
-  };
-
-  if (ng > 0) {
-    load_sz(0);
-    store_sz(0);
-    load_sz(2);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      load_w_part(w0, 0, j);
-      load_w_part(w1, 1, j);
-      load_w_part(w2, 2, j);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      load_x_part(xa, 0, i);
-      load_x_part(xb, 1, i);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) store_x_part(xa, smem, i);
-    __syncthreads();
-    read_a(a0, smem, 0);
-    read_sz(szc, 0, 0);
-    bcur = deq_b(w0, 0, 0, szc[0]);
-    for (int g = 0; g < ng; g += 4) {
-      superstep(g, 0);
-      superstep(g + 1, 1);
-      superstep(g + 2, 2);
-      superstep(g + 3, 3);
-    }
-  }
-
-  const bool partial = a.ksplit > 1;
-  const uint32_t MN = (uint32_t)M * (uint32_t)N;
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int n = n0 + wn * WTN + 32 * j + c32;
-      if (n >= N) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (m < M) {
-          const uint32_t o = (uint32_t)m * (uint32_t)N + (uint32_t)n;
-          if (partial)
-            static_cast<float*>(a.y)[(size_t)slice * MN + o] = acc[i][j][q];
-          else if (a.y_f32)
-            static_cast<float*>(a.y)[o] = acc[i][j][q];
-          else
-            static_cast<f16*>(a.y)[o] = (f16)acc[i][j][q];
-        }
-      }
-    }
-}
-
 // y = sum over slices s = 0..S-1 of ws[s] (fixed order), in the output dtype.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ ws, int S, size_t MN, void* __restrict__ y, int y_f32) {
@@ -944,7 +739,7 @@ splitk_sparse_reduce_kernel(const float* __restrict__ ws, int S, int M, int N, c
 struct GemmPlan {
   int bm, bn;
   // 0: gemm_kernel; 1: gemm_big_kernel 128 x 256; 2 (M <= 64): gemm_big_kernel 64 x 256
-  // with weight windows of four or two super-steps, else gemm_skinny_kernel
+  // with weight windows of four or two super-steps
   int kind;
   int ksplit, k_per_slice;
   // the sparse term is added in the slice sum, from activations transposed into the
@@ -1053,16 +848,6 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MINB>
-static hipError_t launch_skinny(GemmArgs a, hipStream_t stream) {
-  constexpr size_t lds = 2 * (size_t)64 * kBigStride * sizeof(f16) + kBigSzBytes;
-  a.tiles_m = (a.M + 63) / 64;
-  a.tiles_n = (a.N + 255) / 256;
-  const int64_t nblk = (int64_t)a.tiles_m * a.tiles_n * a.ksplit;
-  hipLaunchKernelGGL(gemm_skinny_kernel<MINB>, dim3((unsigned)nblk), dim3(256), lds, stream, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,
@@ -1110,17 +895,16 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.ksplit = p.ksplit;
     a.k_per_slice = p.k_per_slice;
     hipError_t e;
-    // weight windows of WS super-steps need slices and K of a multiple of 2 WS groups
+    // weight windows of WS super-steps need slices and K of a multiple of 2 WS groups;
+    // kind 2 has G and its slices (or the whole K) multiples of four groups, so WS is
+    // four or two
     const int64_t per = p.k_per_slice / 128, G = K / 128;
-    const int ws = per % 8 == 0 && G % 8 == 0 ? 4 : (per % 4 == 0 && G % 4 == 0 ? 2 : 1);
     if (p.kind == 1)
       e = launch_big<128, 256, 1, 4, 2, 1>(a, stream);
-    else if (p.kind == 2 && ws == 4)
+    else if (p.kind == 2 && per % 8 == 0 && G % 8 == 0)
       e = launch_big<64, 256, 1, 4, 2, 4>(a, stream);
-    else if (p.kind == 2 && ws == 2)
-      e = launch_big<64, 256, 1, 4, 2, 2>(a, stream);
     else if (p.kind == 2)
-      e = launch_skinny<2>(a, stream);
+      e = launch_big<64, 256, 1, 4, 2, 2>(a, stream);
     else if (p.bm == 64)
       e = sp_kernel ? launch_tile<64, 256, 1, 4, true>(a, stream) : launch_tile<64, 256, 1, 4, false>(a, stream);
     else
