@@ -33,33 +33,6 @@ __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(
 // out in the order 0,4,1,5,2,6,3,7. A contraction over K does not care about the
 // order inside a chunk of eight, as long as the activations are fed in the same
 // order: perm_x8 reorders eight consecutive activations to match.
-__device__ __forceinline__ uint4 codes_biased(uint32_t w) {
-  uint4 r;
-  r.x = (w & 0x000F000Fu) | 0x64006400u;
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x64006400u;
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x64006400u;
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x64006400u;
-  return r;
-}
-
-// (q - z) for the eight codes of a word, exact in fp16 (|q - z| <= 15):
-// (1024 + q) - (1024 + z) with both operands exact.
-__device__ __forceinline__ f16x8 codes_minus_zero(uint32_t w, f16x2 bias) {
-  uint4 b = codes_biased(w);
-  f16x2 a0 = as_f16x2(b.x) - bias, a1 = as_f16x2(b.y) - bias;
-  f16x2 a2 = as_f16x2(b.z) - bias, a3 = as_f16x2(b.w) - bias;
-  uint4 o = {as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3)};
-  return as_f16x8(o);
-}
-
-// fp16((q - z) * s): one rounding of the exact difference times the scale.
-__device__ __forceinline__ uint4 dequant_word(uint32_t w, f16x2 bias, f16x2 s) {
-  uint4 b = codes_biased(w);
-  f16x2 a0 = (as_f16x2(b.x) - bias) * s, a1 = (as_f16x2(b.y) - bias) * s;
-  f16x2 a2 = (as_f16x2(b.z) - bias) * s, a3 = (as_f16x2(b.w) - bias) * s;
-  uint4 o = {as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3)};
-  return o;
-}
 
 // Eight consecutive fp16 values x0..x7 (two per dword) reordered to
 // x0,x4,x1,x5,x2,x6,x3,x7, the order codes_biased produces.
