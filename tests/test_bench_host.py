@@ -1,0 +1,34 @@
+"""The host side of bench.py on the CPU: the one-GPU refusal, the algorithmic
+units and the oracle baseline record (no GPU involved)."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_units():
+    # packed codes + fp16 scale and zero per group of 128 + x + y, for the decode layer
+    N, K = 11008, 4096
+    assert bench.alg_bytes(1, N, K, 0) == N * K // 2 + N * (K // 128) * 4 + 2 * K + 2 * N == 23983616
+    # the CSR adds 6 bytes per entry and 4 per row pointer
+    assert bench.alg_bytes(16, 4096, 4096, 75497) - bench.alg_bytes(16, 4096, 4096, 0) == 6 * 75497 + 4 * 4097
+    assert bench.alg_flops(2048, 14336, 4096, 0) == 2 * 2048 * 14336 * 4096
+    assert bench.alg_flops(8, 8192, 28672, 117440) == 2 * 8 * 8192 * 28672 + 2 * 8 * 117440
+
+
+def test_cpu_baseline_record():
+    b = bench.cpu_baseline(budget_s=0.05)
+    assert b["kind"] == "oracle" and b["unit"] == "GB/s"
+    assert b["value"] > 0 and b["cores"] >= 1
+    assert set(b["phases_ms"]) == {"quantize_fp32", "dequantize_fp64", "linear_ref"}
+    assert "11008" in b["sample"] and "4096" in b["sample"]
