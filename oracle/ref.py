@@ -189,8 +189,34 @@ def sparse_term(x: np.ndarray, row_ptr, col, val, N: int) -> np.ndarray:
     return out
 
 
-def linear_ref(x, q, s, z, row_ptr=None, col=None, val=None, group: int = GROUP):
-    """y[m, n] = sum_k x[m, k] * w_hat[n, k] + (W_sparse x)[n, m] in float64.
+# --------------------------------------------------------------------------
+# O9: low-rank high-precision branch (DeepCompressor README, SVDQuant section)
+# --------------------------------------------------------------------------
+
+
+def lowrank_term(x, L1, L2) -> np.ndarray:
+    """(x . L1^T) . L2^T in float64, for all rows of x.
+
+    The SVDQuant section of the DeepCompressor README moves outliers from the
+    activations into the weights and lets a high-precision low-rank branch,
+    obtained by SVD, hold the weights' outliers, so that only the residual is
+    quantized to 4 bits; run as a separate kernel that branch costs extra
+    activation traffic, so the engine fuses it into the low-bit kernel.  The
+    pages give neither the rank nor the layout of the factors.  The reading
+    here: W = L2 . L1 + R with fp16 factors L1 [r, K] (the down-projection, one
+    row per component) and L2 [N, r] (the up-projection), applied to the
+    activations as t = x . L1^T and then t . L2^T."""
+    x64 = np.asarray(x).astype(np.float64)
+    L1 = np.asarray(L1).astype(np.float64)
+    L2 = np.asarray(L2).astype(np.float64)
+    if L1.shape[0] == 0:
+        return np.zeros((x64.shape[0], L2.shape[0]), np.float64)
+    return (x64 @ L1.T) @ L2.T
+
+
+def linear_ref(x, q, s, z, row_ptr=None, col=None, val=None, group: int = GROUP, L1=None, L2=None):
+    """y[m, n] = sum_k x[m, k] * w_hat[n, k] + (W_sparse x)[n, m] in float64,
+    plus the low-rank branch (x . L1^T . L2^T)[m, n] when the factors are given.
 
     ``q`` may be the unpacked codes [N, K] (uint8) or the packed words
     [N, K/8] (uint32)."""
@@ -202,10 +228,12 @@ def linear_ref(x, q, s, z, row_ptr=None, col=None, val=None, group: int = GROUP)
     y = np.asarray(x).astype(np.float64) @ W_hat.T
     if row_ptr is not None:
         y += sparse_term(x, row_ptr, col, val, N)
+    if L1 is not None:
+        y += lowrank_term(x, L1, L2)
     return y
 
 
-def linear_rows(x, q, s, z, rows, row_ptr=None, col=None, val=None, group: int = GROUP):
+def linear_rows(x, q, s, z, rows, row_ptr=None, col=None, val=None, group: int = GROUP, L1=None, L2=None):
     """The same as ``linear_ref`` restricted to output channels ``rows``
     (used to check full-size outputs one sample at a time)."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -225,6 +253,8 @@ def linear_rows(x, q, s, z, rows, row_ptr=None, col=None, val=None, group: int =
             a, b = row_ptr[n], row_ptr[n + 1]
             if b > a:
                 y[:, j] += x64[:, col[a:b]] @ v[a:b]
+    if L1 is not None:
+        y += lowrank_term(x, L1, np.asarray(L2)[rows])
     return y
 
 

@@ -339,3 +339,62 @@ def test_quantization_error_within_tolerance_budget():
     w16 = oracle.dequant(L["q"], L["s"], L["z"]).astype(np.float16).astype(np.float64)
     y16 = x.astype(np.float64) @ w16.T
     assert oracle.rel_err_inf(y16, y) < 5e-4
+
+
+# ---------------------------------------------------------------- low-rank branch
+
+
+def test_lowrank_brute_force_rationals():
+    """(x . L1^T) . L2^T against a triple loop in exact rationals."""
+    M, N, K, r = 2, 5, 24, 3
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    L1 = rng.standard_normal((r, K)).astype(np.float16)
+    L2 = rng.standard_normal((N, r)).astype(np.float16)
+    y = oracle.lowrank_term(x, L1, L2)
+    assert y.shape == (M, N)
+    for m in range(M):
+        for n in range(N):
+            ex = sum(Fraction(float(L2[n, j])) * sum(Fraction(float(x[m, k])) * Fraction(float(L1[j, k]))
+                                                      for k in range(K)) for j in range(r))
+            assert abs(y[m, n] - float(ex)) <= 1e-12 * max(1.0, abs(float(ex)))
+
+
+def test_lowrank_equals_the_dense_product_of_its_factors():
+    """In integers, applying the branch as two projections equals multiplying by
+    the dense matrix L2 . L1 (a transposed or swapped factor breaks this on
+    these non-square shapes)."""
+    M, N, K, r = 3, 7, 256, 32
+    L1, L2 = workloads.integer_lowrank_factors(72, r, N, K, nnz_per_row=40)
+    x = np.random.default_rng(73).integers(-4, 5, size=(M, K)).astype(np.float16)
+    W_lr = L2.astype(np.int64) @ L1.astype(np.int64)          # [N, K]
+    want = x.astype(np.int64) @ W_lr.T
+    assert np.array_equal(oracle.lowrank_term(x, L1, L2), want.astype(np.float64))
+    # one-hot activations read a column of L2 . L1
+    for k in (0, 5, 255):
+        e = np.zeros((1, K), np.float16)
+        e[0, k] = 1.0
+        assert np.array_equal(oracle.lowrank_term(e, L1, L2)[0], W_lr[:, k].astype(np.float64))
+
+
+def test_lowrank_in_the_linear_layer():
+    """The branch adds to the dense and sparse terms in linear_ref and in
+    linear_rows, and rank 0 adds nothing."""
+    M, N, K, r = 3, 40, 256, 32
+    W = workloads.random_weights(74, N, K)
+    x = workloads.random_x(75, M, K)
+    L = oracle.quantize_layer(W, 25)
+    L1, L2 = workloads.lowrank_factors(76, r, N, K)
+    base = oracle.linear_ref(x, L["packed"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    full = oracle.linear_ref(x, L["packed"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"], L1=L1, L2=L2)
+    # the branch computed column by column from its definition
+    t = [[sum(float(x[m, k]) * float(L1[j, k]) for k in range(K)) for j in range(r)] for m in range(M)]
+    for m in range(M):
+        for n in (0, 17, 39):
+            lr = sum(t[m][j] * float(L2[n, j]) for j in range(r))
+            assert abs(full[m, n] - base[m, n] - lr) <= 1e-9 * max(1.0, abs(lr))
+    rows = [0, 7, 39, 13]
+    ys = oracle.linear_rows(x, L["packed"], L["s"], L["z"], rows, L["row_ptr"], L["col"], L["val"], L1=L1, L2=L2)
+    assert np.allclose(ys, full[:, rows], rtol=1e-13, atol=1e-13)
+    empty = oracle.lowrank_term(x, np.zeros((0, K), np.float16), np.zeros((N, 0), np.float16))
+    assert empty.shape == (M, N) and not empty.any()

@@ -168,3 +168,28 @@ def integer_case(seed: int, M: int, N: int, K: int, nnz_per_row: int = 3, group:
     col = np.concatenate(cols) if cols else np.zeros(0, np.int32)
     val = np.concatenate(vals) if vals else np.zeros(0, np.float16)
     return x, q, s, z, row_ptr, col, val
+
+
+def lowrank_factors(seed: int, r: int, N: int, K: int, sigma_up: float = 0.2):
+    """Random fp16 factors of a rank-r branch: L1 [r, K] ~ N(0, 1/K) (so that
+    x . L1^T stays of unit size for unit activations) and L2 [N, r] ~ N(0,
+    sigma_up^2).  No rank or factor values are given by the pages; these only
+    give the branch a size comparable to the dense product."""
+    rng = np.random.default_rng(seed)
+    L1 = (rng.standard_normal((r, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K))).astype(np.float16)
+    L2 = (rng.standard_normal((N, r), dtype=np.float32) * np.float32(sigma_up)).astype(np.float16)
+    return L1, L2
+
+
+def integer_lowrank_factors(seed: int, r: int, N: int, K: int, nnz_per_row: int = 256):
+    """Integer factors for the exact case: L1 [r, K] in {-1, 0, 1} with at most
+    nnz_per_row non-zeros per row and L2 [N, r] in {-2..2}.  With activations in
+    {-4..4} and nnz_per_row <= 256, every |x . L1^T| <= 1024 is an integer that
+    fp16 holds exactly, and every partial sum of the branch is exact in fp32."""
+    rng = np.random.default_rng(seed)
+    L1 = np.zeros((r, K), np.float16)
+    for j in range(r):
+        c = rng.choice(K, min(nnz_per_row, K), replace=False)
+        L1[j, c] = rng.choice([-1, 1], size=c.size).astype(np.float16)
+    L2 = rng.integers(-2, 3, size=(N, r)).astype(np.float16)
+    return L1, L2
