@@ -149,6 +149,38 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K,
                             int64_t nnz, void* y, int32_t y_dtype, int32_t kernel,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace wq_linear_lowrank needs: t = x . L1^T [M, r] fp16,
+ * the fp32 partials of its K chunks, and the split-K workspace of
+ * wq_linear_workspace_bytes(M, N, K). 0 for invalid sizes (r must be a multiple
+ * of 32 up to 256). */
+size_t wq_linear_lowrank_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+
+/*
+ * wq_linear_lowrank - wq_linear_sparse_kernel plus a rank-r high-precision branch
+ * (SVDQuant section of the DeepCompressor README: a low-rank branch holds the
+ * weights' outliers while the residual is quantized, fused with the low-bit
+ * kernel rather than run as a separate pass):
+ *   y = x . dequant(packed)^T + W_sparse . x + (x . L1^T) . L2^T,
+ * i.e. W = L2 . L1 + residual.
+ *  L1  [r, K] fp16, the down-projection (one row per component), 16-byte aligned.
+ *  L2  [N, r] fp16, the up-projection, 16-byte aligned.
+ *  r   a multiple of 32 up to 256 (WQ_ERR_UNSUPPORTED otherwise; < 1: WQ_ERR_SHAPE).
+ *  row_ptr / col / val / nnz as in wq_linear_sparse; row_ptr may be NULL when
+ *  nnz == 0 (no sparse term). kernel as in wq_linear_sparse_kernel.
+ *  workspace: required, wq_linear_lowrank_workspace_bytes(M, N, K, r) bytes,
+ *  16-byte aligned (WQ_ERR_WORKSPACE otherwise); contents on entry do not matter.
+ * t = x . L1^T is accumulated in fp32 and rounded once to fp16 (it is an MFMA
+ * operand); each output tile then adds t . L2^T to its fp32 accumulators before
+ * the one store of y. Deterministic, like the other linear entry points.
+ */
+int wq_linear_lowrank(const uint16_t* x, int64_t M, int64_t K,
+                      const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                      int64_t N, int32_t group,
+                      const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
+                      const uint16_t* L1, const uint16_t* L2, int64_t r,
+                      void* y, int32_t y_dtype, int32_t kernel,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* The kernel WQ_KERNEL_AUTO picks for M rows (WQ_KERNEL_GEMV or WQ_KERNEL_GEMM). */
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K);
 

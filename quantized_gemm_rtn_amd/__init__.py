@@ -10,6 +10,8 @@ Entry points (the same names as the C ABI, without the ``wq_`` prefix):
 * ``pack(codes)``                eight codes per 32-bit word
 * ``linear(x, packed, scales, zeros)``
 * ``linear_sparse(x, packed, scales, zeros, row_ptr, col, val)``
+* ``linear_lowrank(x, packed, scales, zeros, L1, L2, row_ptr, col, val)``
+  the same plus a rank-r fp16 branch (x . L1^T) . L2^T
 """
 from __future__ import annotations
 
@@ -37,6 +39,9 @@ SIGNATURES = {
                                         _vp, _i32, _vp, _sz, _vp]),
     "wq_linear_sparse_kernel": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
                                                _vp, _i32, _i32, _vp, _sz, _vp]),
+    "wq_linear_lowrank_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "wq_linear_lowrank": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
+                                         _vp, _vp, _i64, _vp, _i32, _i32, _vp, _sz, _vp]),
     "wq_auto_kernel": (ctypes.c_int, [_i64, _i64, _i64]),
     "wq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -185,6 +190,61 @@ def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, ou
 def linear(x, packed, scales, zeros, out_dtype=None, kernel: str = "auto", out=None, group: int = GROUP,
            workspace=None):
     return linear_sparse(x, packed, scales, zeros, None, None, None, out_dtype, kernel, out, group, workspace)
+
+
+def linear_lowrank_workspace_bytes(M, N, K, r):
+    return int(load().wq_linear_lowrank_workspace_bytes(M, N, K, r))
+
+
+def linear_lowrank(x, packed, scales, zeros, L1, L2, row_ptr=None, col=None, val=None, out_dtype=None,
+                   kernel: str = "auto", out=None, group: int = GROUP, workspace=None):
+    """y = x . dequant(packed, scales, zeros)^T (+ W_sparse x when CSR is given)
+    + (x . L1^T) . L2^T, with L1 [r, K] and L2 [N, r] fp16 (r a multiple of 32).
+
+    ``workspace`` (uint8 device tensor of ``linear_lowrank_workspace_bytes``
+    bytes) is allocated per call when omitted."""
+    import torch
+    lib = load()
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    _need(x, torch.float16, "x")
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.float16, "zeros")
+    _need(L1, torch.float16, "L1")
+    _need(L2, torch.float16, "L2")
+    M, K = x.shape
+    N = packed.shape[0]
+    r = L1.shape[0]
+    if packed.shape[1] * 8 != K or scales.shape != (N, K // group) or zeros.shape != scales.shape:
+        raise ValueError("inconsistent shapes")
+    if L1.shape != (r, K) or L2.shape != (N, r):
+        raise ValueError("L1 must be [r, K] and L2 [N, r]")
+    nnz = 0
+    if row_ptr is not None:
+        _need(row_ptr, torch.int32, "row_ptr")
+        if row_ptr.numel() != N + 1:
+            raise ValueError("row_ptr must have N+1 entries")
+        nnz = int(col.numel()) if col is not None else 0
+        if nnz:
+            _need(col, torch.int32, "col")
+            _need(val, torch.float16, "val")
+    if out_dtype not in (torch.float16, torch.float32):
+        raise TypeError("out_dtype must be float16 or float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    y_dtype = 1 if out_dtype == torch.float32 else 0
+    if workspace is None:
+        nbytes = int(lib.wq_linear_lowrank_workspace_bytes(max(M, 1), N, K, r))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    rc = lib.wq_linear_lowrank(_p(x), M, K, _p(packed), _p(scales), _p(zeros), N, group,
+                               _p(row_ptr) if nnz else None, _p(col) if nnz else None, _p(val) if nnz else None,
+                               nnz, _p(L1), _p(L2), r, _p(out), y_dtype, KERNELS[kernel], _p(workspace), wbytes,
+                               _stream(x))
+    _check("wq_linear_lowrank", rc)
+    return out
 
 
 def auto_kernel(M, N, K) -> str:

@@ -65,7 +65,35 @@ struct GemmArgs {
   int ksplit;        // number of K slices (1: no split)
   int k_per_slice;   // multiple of kBK
   int tiles_m, tiles_n;
+  // low-rank branch: t [M][lr_r] and L2 [N][lr_r] fp16, lr_r = 0 for none
+  const f16* lr_t;
+  const f16* lr_up;
+  int lr_r;
 };
+
+// Up-projection of a low-rank branch for a wave's MT x NT subtiles of 32 x 32:
+// acc[i][j] += t . L2^T with rows of t [M][r] in A and rows of L2 [N][r] in B, 16
+// of the rank per 32x32x16 MFMA (the same output layout as the weights' MFMAs);
+// added by the first K slice only. Rows past M or N read the last row and are
+// never stored.
+template <int MT, int NT>
+__device__ __forceinline__ void lowrank_add32(f32x16 (&acc)[MT][NT], const f16* t, const f16* up, int r, int M,
+                                              int N, int mbase, int nbase, int lane) {
+  const int h = lane >> 5, c32 = lane & 31;
+  for (int s = 0; s < r; s += 16) {
+    f16x8 av[MT], bv[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      av[i] = as_f16x8(*reinterpret_cast<const uint4*>(t + (size_t)min(mbase + 32 * i + c32, M - 1) * r + s + 8 * h));
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      bv[j] = as_f16x8(*reinterpret_cast<const uint4*>(up + (size_t)min(nbase + 32 * j + c32, N - 1) * r + s + 8 * h));
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[i][j] = mfma_32x32x16(av[i], bv[j], acc[i][j]);
+  }
+}
 
 // Two waves per SIMD (two blocks per CU): the blocks run out of phase, so one
 // block's waits on memory and barriers are covered by the other's MFMAs.
@@ -279,6 +307,7 @@ gemm_kernel(GemmArgs a) {
     __syncthreads();
   }
 
+  if (a.lr_r > 0 && slice == 0) lowrank_add32<MT, NT>(acc, a.lr_t, a.lr_up, a.lr_r, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
   // store: the final y, or this slice's fp32 partial tile
   const bool partial = a.ksplit > 1;
 #pragma unroll
@@ -578,6 +607,7 @@ gemm_big_kernel(GemmArgs a) {
     }
   }
 
+  if (a.lr_r > 0 && slice == 0) lowrank_add32<MT, NT>(acc, a.lr_t, a.lr_up, a.lr_r, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
   // store: the final y, or this slice's fp32 partial tile
   const bool partial = a.ksplit > 1;
   const uint32_t MN = (uint32_t)M * (uint32_t)N;
@@ -851,7 +881,7 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t stream) {
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+                       size_t workspace_bytes, const LowRank& lr, hipStream_t stream) {
   constexpr int64_t kRowsPerLaunch = (int64_t)1 << 20;  // keeps the block count within int range
   for (int64_t m = 0; m < M; m += kRowsPerLaunch) {
     const int64_t mc = M - m < kRowsPerLaunch ? M - m : kRowsPerLaunch;
@@ -894,6 +924,9 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.y_f32 = y_f32;
     a.ksplit = p.ksplit;
     a.k_per_slice = p.k_per_slice;
+    a.lr_t = lr.r > 0 ? reinterpret_cast<const f16*>(lr.t) + m * lr.r : nullptr;
+    a.lr_up = reinterpret_cast<const f16*>(lr.up);
+    a.lr_r = (int)lr.r;
     hipError_t e;
     // weight windows of WS super-steps need slices and K of a multiple of 2 WS groups;
     // kind 2 has G and its slices (or the whole K) multiples of four groups, so WS is

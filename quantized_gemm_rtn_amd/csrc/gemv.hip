@@ -270,12 +270,43 @@ __device__ __forceinline__ void reduce_store(f32x4 acc, int wave, int lane, int 
 }
 
 // ---------------------------------------------------------------------------
+// Up-projection of a low-rank branch for a wave's NT 16-channel tiles:
+// acc[j] += t . L2^T, rows m0 .. m0 + 15 of t [M][r] in A and the tile's rows of
+// L2 [N][r] in B, 32 of the rank per 16x16x32 MFMA (the same output layout as the
+// weights' MFMAs). Four steps' loads go out before their MFMAs; rows past M or N
+// read the last row and are never stored.
+template <int NT>
+__device__ __forceinline__ void lowrank_add16(f32x4 (&acc)[NT], const f16* t, const f16* up, int r, int M, int N,
+                                              int m0, int n0, int lane) {
+  const int q = lane & 15, h = lane >> 4;
+  const f16* ta = t + (size_t)min(m0 + q, M - 1) * r + 8 * h;
+  const f16* ub[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) ub[j] = up + (size_t)min(n0 + 16 * j + q, N - 1) * r + 8 * h;
+  for (int s = 0; s < r; s += 128) {
+    uint4 a[4], b[4][NT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ss = min(s + 32 * u, r - 32);
+      a[u] = *reinterpret_cast<const uint4*>(ta + ss);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b[u][j] = *reinterpret_cast<const uint4*>(ub[j] + ss);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s + 32 * u < r)  // wave-uniform
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = mfma_16x16x32(as_f16x8(a[u]), as_f16x8(b[u][j]), acc[j]);
+  }
+}
+
 template <int KW, int D, int XC, int SZV, int MR, bool SP>
 __global__ void __launch_bounds__(64 * KW)
 gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
                 const f16* __restrict__ scales, const f16* __restrict__ zeros, int N,
                 const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-                const f16* __restrict__ val, void* __restrict__ y, int y_f32) {
+                const f16* __restrict__ val, void* __restrict__ y, int y_f32, const f16* __restrict__ lr_t,
+                const f16* __restrict__ lr_up, int lr_r) {
   constexpr int T = 64 * KW;
   extern __shared__ __align__(16) char smem[];
   const int t = threadIdx.x;
@@ -486,6 +517,12 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
       for (int b = 0; b < kSparseBatch; ++b) add(more.c[b], more.weight(b, e, sp_e1));
     }
   }
+  // low-rank branch, once per output tile (wave 0, before the waves' sum)
+  if (lr_r > 0 && wave == 0) {
+    f32x4 a1[1] = {acc};
+    lowrank_add16<1>(a1, lr_t, lr_up, lr_r, M, N, m0, n0, lane);
+    acc = a1[0];
+  }
   reduce_store<KW>(acc, wave, lane, m0, mrows, n, N, y, y_f32);
 }
 
@@ -502,7 +539,8 @@ __global__ void __launch_bounds__(64 * KW)
 gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
                  const f16* __restrict__ scales, const f16* __restrict__ zeros, int N,
                  const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-                 const f16* __restrict__ val, void* __restrict__ y, int y_f32) {
+                 const f16* __restrict__ val, void* __restrict__ y, int y_f32, const f16* __restrict__ lr_t,
+                 const f16* __restrict__ lr_up, int lr_r) {
   constexpr int T = 64 * KW;
   constexpr int R = 4 * XL;          // rows staged per group
   constexpr int kRowHalves = 136;    // 128 + 8
@@ -658,6 +696,8 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
       }
     }
   }
+  // low-rank branch, once per output tile (wave 0, before the waves' sum)
+  if (lr_r > 0 && wave == 0) lowrank_add16<NT>(acc, lr_t, lr_up, lr_r, M, N, m0, n0, lane);
   reduce_store_tiles<KW, NT>(acc, wave, lane, m0, mrows, n0 + r, N, y, y_f32);
 }
 
@@ -666,7 +706,7 @@ template <typename Kern>
 static hipError_t launch_rows(Kern kern, size_t lds, int cols, const uint16_t* x, int64_t M, int64_t K,
                               const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N,
                               const int32_t* row_ptr, const int32_t* col, const uint16_t* val, void* y, int y_f32,
-                              hipStream_t stream, size_t* lds_set) {
+                              const LowRank& lr, hipStream_t stream, size_t* lds_set) {
   if (lds > 65536 && lds > *lds_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -681,7 +721,9 @@ static hipError_t launch_rows(Kern kern, size_t lds, int cols, const uint16_t* x
     hipLaunchKernelGGL(kern, grid, dim3(64 * kGemvWaves), lds, stream, reinterpret_cast<const f16*>(x) + m * K,
                        (int)mc, (int)K, packed, reinterpret_cast<const f16*>(scales),
                        reinterpret_cast<const f16*>(zeros), (int)N, row_ptr, col, reinterpret_cast<const f16*>(val),
-                       static_cast<char*>(y) + (size_t)(m * N) * ysz, y_f32);
+                       static_cast<char*>(y) + (size_t)(m * N) * ysz, y_f32,
+                       lr.r > 0 ? reinterpret_cast<const f16*>(lr.t) + m * lr.r : nullptr,
+                       reinterpret_cast<const f16*>(lr.up), (int)lr.r);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -691,28 +733,31 @@ static hipError_t launch_rows(Kern kern, size_t lds, int cols, const uint16_t* x
 template <int XC, int SZV, int MR, bool SP>
 static hipError_t launch_lds(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
-                             const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
+                             const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
+                             hipStream_t stream) {
   static size_t lds_set = 0;
   const int64_t G = K / kGroup, mrows = M < 16 ? M : 16, SR = MR == 1 ? 1 : 4 * ((mrows + 3) / 4);
   const size_t lds = (SZV == kSzInRegs ? 0 : (size_t)16 * (G + 1) * 4) + (size_t)mrows * K * 2 +
                      (size_t)2 * G * SR * 4;
   return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR, SP>, lds, 16, x, M, K, packed, scales, zeros, N,
-                     row_ptr, col, val, y, y_f32, stream, &lds_set);
+                     row_ptr, col, val, y, y_f32, lr, stream, &lds_set);
 }
 
 template <int XL, int NT, int SZV, bool SP>
 static hipError_t launch_ring(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                               const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
-                              const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
+                              const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
+                              hipStream_t stream) {
   static size_t lds_set = 0;
   const size_t lds = (size_t)NT * 16 * (K / kGroup + 1) * 4 + (size_t)kGemvWaves * 4 * XL * 136 * 2;
   return launch_rows(gemv_ring_kernel<kGemvWaves, kGemvRingDepth, XL, NT, SZV, SP>, lds, 16 * NT, x, M, K, packed,
-                     scales, zeros, N, row_ptr, col, val, y, y_f32, stream, &lds_set);
+                     scales, zeros, N, row_ptr, col, val, y, y_f32, lr, stream, &lds_set);
 }
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
-                       const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
+                       const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
+                       hipStream_t stream) {
   const int64_t G = K / kGroup;
   // a CSR is passed only with nnz >= 1: its kernels may read entry 0 of an empty row
   const bool sp = row_ptr != nullptr;
@@ -741,7 +786,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   // (from M = 3 on, staging per wave and group is faster, even where x would fit)
   const int xc = mrows_max * K > kXLdsMaxHalves || mrows_max > 2 ? 0
                  : xloads <= 1 ? 1 : xloads <= 2 ? 2 : xloads <= 4 ? 4 : xloads <= 8 ? 8 : 16;
-#define WQ_ARGS x, M, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, stream
+#define WQ_ARGS x, M, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, lr, stream
 #define WQ_LDS(XC, SV, MR)                                 \
   if (xc == XC && sz_mode == SV && mr == MR) {             \
     if (sp) return launch_lds<XC, SV, MR, true>(WQ_ARGS);  \

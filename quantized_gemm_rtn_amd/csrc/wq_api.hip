@@ -12,6 +12,10 @@ namespace {
 
 constexpr int64_t kGroup = 128;
 constexpr int64_t kMax32 = (int64_t)1 << 31;  // element counts must stay below 2^31
+constexpr int64_t kMaxRank = 256;             // rank of the low-rank branch: multiples of 32 up to this
+
+// t [M][r] fp16 of the low-rank branch, at the start of its workspace
+size_t lowrank_t_bytes(int64_t M, int64_t r) { return ((size_t)M * r * 2 + 255) / 256 * 256; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -124,10 +128,52 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K, const uint3
   const int32_t* rp = nnz > 0 ? row_ptr : nullptr;  // nnz == 0: the dense product
   hipError_t e;
   if (kernel == WQ_KERNEL_GEMV)
-    e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, as_stream(stream));
+    e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, wq::LowRank{},
+                        as_stream(stream));
   else
     e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32,
                         workspace != nullptr && aligned(workspace, 16) ? workspace : nullptr, workspace_bytes,
+                        wq::LowRank{}, as_stream(stream));
+  return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+}
+
+size_t wq_linear_lowrank_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) return 0;
+  if (N >= kMax32 / K || M >= kMax32 / K || M >= kMax32 / N) return 0;
+  if (r < 32 || r % 32 != 0 || r > kMaxRank) return 0;
+  return lowrank_t_bytes(M, r) + wq::lowrank_partial_bytes(M, K, r) + wq::gemm_workspace_bytes(M, N, K);
+}
+
+int wq_linear_lowrank(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
+                      const uint16_t* zeros, int64_t N, int32_t group, const int32_t* row_ptr, const int32_t* col,
+                      const uint16_t* val, int64_t nnz, const uint16_t* L1, const uint16_t* L2, int64_t r, void* y,
+                      int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                                   kernel);
+  if (rc != WQ_OK) return rc;
+  if (!L1 || !L2) return WQ_ERR_NULL;
+  if (r < 1) return WQ_ERR_SHAPE;
+  if (r % 32 != 0 || r > kMaxRank) return WQ_ERR_UNSUPPORTED;
+  if (!aligned(L1, 16) || !aligned(L2, 16)) return WQ_ERR_ALIGN;
+  if (M == 0) return WQ_OK;
+  const size_t need = wq_linear_lowrank_workspace_bytes(M, N, K, r);
+  if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return WQ_ERR_WORKSPACE;
+  // workspace: t | down-projection partials | the GEMM's split-K workspace
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* t = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(ws + lowrank_t_bytes(M, r));
+  char* gws = ws + lowrank_t_bytes(M, r) + wq::lowrank_partial_bytes(M, K, r);
+  const size_t gws_bytes = workspace_bytes - (size_t)(gws - ws);
+  if (kernel == WQ_KERNEL_AUTO) kernel = wq_auto_kernel(M, N, K);
+  const int y_f32 = y_dtype == WQ_F32;
+  const int32_t* rp = nnz > 0 ? row_ptr : nullptr;  // nnz == 0: no sparse term
+  const wq::LowRank lr{t, L2, r};
+  hipError_t e = wq::launch_lowrank_down(x, M, K, L1, r, part, t, as_stream(stream));
+  if (e != hipSuccess) return WQ_ERR_HIP;
+  if (kernel == WQ_KERNEL_GEMV)
+    e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, lr, as_stream(stream));
+  else
+    e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32, gws, gws_bytes, lr,
                         as_stream(stream));
   return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
 }

@@ -27,9 +27,24 @@ hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int6
                            uint16_t* scales, uint16_t* zeros, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream);
 
+// The up-projection of a low-rank branch, added to every output tile before its
+// store: t [M, r] fp16 (the down-projection x . L1^T) and L2 [N, r] fp16; r = 0: none.
+struct LowRank {
+  const uint16_t* t = nullptr;
+  const uint16_t* up = nullptr;
+  int64_t r = 0;
+};
+
+// The down-projection t = fp16(x . L1^T) of a low-rank branch (r a multiple of 32),
+// through fp32 partials of K chunks in `part` (lowrank_partial_bytes(M, K, r)).
+size_t lowrank_partial_bytes(int64_t M, int64_t K, int64_t r);
+hipError_t launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* L1, int64_t r,
+                               float* part, uint16_t* t, hipStream_t stream);
+
 hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
-                       const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream);
+                       const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
+                       hipStream_t stream);
 // The GEMM splits K through `workspace` (fp32 partials) when its tile grid alone
 // cannot fill the GPU and the workspace holds gemm_workspace_bytes(M, N, K);
 // otherwise it runs unsplit.
@@ -37,6 +52,6 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+                       size_t workspace_bytes, const LowRank& lr, hipStream_t stream);
 
 }  // namespace wq

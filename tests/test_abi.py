@@ -142,3 +142,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(wq, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         wq.load()
+
+
+def lowrank(lib, x=A, M=1, K=256, packed=A2, scales=A3, zeros=A4, N=64, group=128, row_ptr=None, col=None,
+            val=None, nnz=0, L1=A5, L2=A, r=32, y=A5, y_dtype=0, kernel=0, ws=None, ws_bytes=0):
+    return lib.wq_linear_lowrank(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, L1, L2, r, y,
+                                 y_dtype, kernel, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L1=None), -1), (dict(L2=None), -1), (dict(x=None), -1), (dict(nnz=4), -1),
+    (dict(r=0), -2), (dict(r=-32), -2), (dict(M=-1), -2),
+    (dict(r=16), -4), (dict(r=48), -4), (dict(r=288), -4), (dict(group=64), -4),
+    (dict(L1=MIS), -3), (dict(L2=MIS), -3),
+    (dict(), -6), (dict(ws=A, ws_bytes=16), -6), (dict(ws=MIS, ws_bytes=1 << 30), -6),
+])
+def test_lowrank_validation(lib, kw, status):
+    assert lowrank(lib, **kw) == status
+
+
+def test_lowrank_workspace_and_empty_batch(lib):
+    # t [1, 32] fp16 and the fp32 partials of the 4 K chunks of 1024 channels
+    assert lib.wq_linear_lowrank_workspace_bytes(1, 11008, 4096, 32) >= 64 + 4 * 32 * 4
+    assert lib.wq_linear_lowrank_workspace_bytes(512, 8192, 28672, 64) >= \
+        lib.wq_linear_workspace_bytes(512, 8192, 28672) + 512 * 64 * 2 + 28 * 512 * 64 * 4
+    for bad in ((1, 64, 256, 16), (1, 64, 256, 0), (0, 64, 256, 32), (1, 64, 100, 32), (1, 64, 256, 512)):
+        assert lib.wq_linear_lowrank_workspace_bytes(*bad) == 0
+    # an empty batch launches nothing and needs no workspace
+    assert lowrank(lib, M=0, x=None, y=None) == 0
