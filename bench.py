@@ -20,7 +20,8 @@ the same way (at least 200 launches and 20 ms, from one timed replay of 20).
 Printed: ONE JSON line with the metric (GB/s, algorithmic bytes), the roofline
 of the dominant kernel, the CPU oracle baseline, and the other workloads
 (batched decode + sparse, prefill, the 70B down-projection M sweep and one GPU's
-shard of it), and, as context, torch's device copy of the same byte count.
+shard of it, the decode and prefill layers with a rank-32 low-rank branch), and,
+as context, torch's device copy of the same byte count.
 """
 from __future__ import annotations
 
@@ -44,23 +45,24 @@ MFMA_F16_PEAK_TFS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 ROTATE_BYTES = 1 << 30
 
 
-def alg_bytes(M, N, K, nnz, y_bytes=2):
-    """Bytes the method must move: packed codes, fp16 scale+zero, CSR, x, y."""
+def alg_bytes(M, N, K, nnz, y_bytes=2, rank=0):
+    """Bytes the method must move: packed codes, fp16 scale+zero, CSR, the fp16
+    low-rank factors, x, y."""
     csr = (6 * nnz + 4 * (N + 1)) if nnz else 0
-    return N * K // 2 + N * (K // 128) * 4 + csr + M * K * 2 + M * N * y_bytes
+    return N * K // 2 + N * (K // 128) * 4 + csr + 2 * rank * (K + N) + M * K * 2 + M * N * y_bytes
 
 
-def alg_flops(M, N, K, nnz):
-    return 2 * M * N * K + 2 * M * nnz
+def alg_flops(M, N, K, nnz, rank=0):
+    return 2 * M * N * K + 2 * M * nnz + 2 * M * rank * (K + N)
 
 
 class Layer:
     """A quantized layer on the GPU, produced by the library's own quantizer."""
 
-    def __init__(self, wq, torch, index, M, K=None):
+    def __init__(self, wq, torch, index, M, K=None, rank=0):
         W, x, cfg = workloads.make(index, M=M, K=K)
         N, K = W.shape
-        self.N, self.K, self.M = N, K, M
+        self.N, self.K, self.M, self.rank = N, K, M, rank
         self.sparse_k = workloads.sparse_k_for(cfg, N, K)
         Wd = torch.from_numpy(W).cuda()
         q = wq.quantize_rtn(Wd, sparse_k=self.sparse_k)
@@ -69,11 +71,16 @@ class Layer:
         self.row_ptr, self.col, self.val = q["row_ptr"], q["col"], q["val"]
         del q, Wd
         self.x = torch.from_numpy(x.view(np.int16).copy()).cuda().view(torch.float16)
+        if rank:
+            L1, L2 = workloads.lowrank_factors(index + 100 * M, rank, N, K)
+            self.L1 = torch.from_numpy(L1.view(np.int16).copy()).cuda().view(torch.float16)
+            self.L2 = torch.from_numpy(L2.view(np.int16).copy()).cuda().view(torch.float16)
+            self.ws_bytes = wq.linear_lowrank_workspace_bytes(M, N, K, rank)
         torch.cuda.synchronize()
 
     def sets(self, torch, rotate_bytes):
         """R independent copies of every input/output, R * bytes >= rotate_bytes."""
-        nb = alg_bytes(self.M, self.N, self.K, self.sparse_k)
+        nb = alg_bytes(self.M, self.N, self.K, self.sparse_k, rank=self.rank)
         R = max(1, min(64, math.ceil(rotate_bytes / nb)))
         out = []
         for r in range(R):
@@ -81,13 +88,20 @@ class Layer:
                      zeros=self.zeros.clone(), row_ptr=self.row_ptr.clone(), col=self.col.clone(),
                      val=self.val.clone(),
                      y=torch.empty((self.M, self.N), dtype=torch.float16, device="cuda"))
+            if self.rank:
+                s.update(L1=self.L1.clone(), L2=self.L2.clone(),
+                         ws=torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda"))
             out.append(s)
         return out
 
 
 def launch(wq, s, kernel="auto"):
-    wq.linear_sparse(s["x"], s["packed"], s["scales"], s["zeros"], s["row_ptr"], s["col"], s["val"],
-                     out=s["y"], kernel=kernel)
+    if "L1" in s:
+        wq.linear_lowrank(s["x"], s["packed"], s["scales"], s["zeros"], s["L1"], s["L2"], s["row_ptr"], s["col"],
+                          s["val"], out=s["y"], kernel=kernel, workspace=s["ws"])
+    else:
+        wq.linear_sparse(s["x"], s["packed"], s["scales"], s["zeros"], s["row_ptr"], s["col"], s["val"],
+                         out=s["y"], kernel=kernel)
 
 
 def time_launches(wq, torch, sets, steps, warmup, kernel="auto", repeats=5):
@@ -128,18 +142,20 @@ def replay_length(wq, torch, sets, kernel, min_ms=25.0, min_steps=200, max_steps
     return int(min(max_steps, max(min_steps, math.ceil(min_ms / t))))
 
 
-def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5):
-    """steps = None: enough launches per replay for >= 20 ms (and >= 200 launches)."""
-    L = Layer(wq, torch, index, M, K)
+def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5, rank=0):
+    """steps = None: enough launches per replay for >= 20 ms (and >= 200 launches);
+    rank > 0: with a low-rank branch of that rank."""
+    L = Layer(wq, torch, index, M, K, rank)
     sets = L.sets(torch, ROTATE_BYTES)
     if steps is None:
         steps = replay_length(wq, torch, sets, kernel)
     runs = time_launches(wq, torch, sets, steps, warmup, kernel, repeats=replays)
     ms = float(np.median(runs))
-    nb = alg_bytes(M, L.N, L.K, L.sparse_k)
-    nf = alg_flops(M, L.N, L.K, L.sparse_k)
+    nb = alg_bytes(M, L.N, L.K, L.sparse_k, rank=rank)
+    nf = alg_flops(M, L.N, L.K, L.sparse_k, rank=rank)
     used = kernel if kernel != "auto" else wq.auto_kernel(M, L.N, L.K)
-    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, kernel=used, steps=steps, us_per_launch=ms * 1e3,
+    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, rank=rank, kernel=used, steps=steps,
+               us_per_launch=ms * 1e3,
                us_p10=float(np.percentile(runs, 10)) * 1e3, us_p90=float(np.percentile(runs, 90)) * 1e3,
                replays=len(runs),
                alg_bytes=nb, alg_flops=nf, GBps=nb / (ms * 1e-3) / 1e9, TFLOPs=nf / (ms * 1e-3) / 1e12,
@@ -292,7 +308,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--replays", type=int, default=5, help="timed replays per workload (median, p10, p90)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel],... "
+    ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel[:K[:rank]]],... "
                     "(default: the batched-decode, prefill and 70B-sweep set)")
     ap.add_argument("--no-offline", action="store_true", help="skip timing the offline quantizer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -328,21 +344,25 @@ def main():
             for item in args.workloads.split(","):
                 f = item.split(":")
                 plan.append((int(f[0]), int(f[1]), f[2] if len(f) > 2 and f[2] else "auto",
-                             int(f[3]) if len(f) > 3 else None))
+                             int(f[3]) if len(f) > 3 and f[3] else None, int(f[4]) if len(f) > 4 else 0))
         else:
-            plan = [(3, 16, "auto", None), (4, 2048, "auto", None), (5, 1, "auto", None), (5, 8, "auto", None),
-                    (5, 64, "auto", None), (5, 512, "auto", None)]
+            plan = [(3, 16, "auto", None, 0), (4, 2048, "auto", None, 0), (5, 1, "auto", None, 0),
+                    (5, 8, "auto", None, 0), (5, 64, "auto", None, 0), (5, 512, "auto", None, 0)]
             # the other kernel on either side of the crossover
             for M in (8, 64):
                 other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
-                plan.append((5, M, other, None))
+                plan.append((5, M, other, None, 0))
             # one GPU's shard of the 70B down-projection split over 8 GPUs along K
             # (K / 8 = 3584 input channels, 28 groups)
-            plan += [(5, 1, "auto", 3584), (5, 512, "auto", 3584)]
-        for index, M, kern, Kov in plan:
-            r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov, replays=args.replays)
+            plan += [(5, 1, "auto", 3584, 0), (5, 512, "auto", 3584, 0)]
+            # the decode and prefill layers with a rank-32 low-rank branch
+            plan += [(2, 1, "auto", None, 32), (4, 2048, "auto", None, 32)]
+        for index, M, kern, Kov, rank in plan:
+            r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov, replays=args.replays,
+                        rank=rank)
             rows.append(r)
-            print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov} {r['kernel']:4s} "
+            print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov}{' r=%d' % rank if rank else ''} "
+                  f"{r['kernel']:4s} "
                   f"{r['us_per_launch']:9.2f} us  "
                   f"{r['GBps']:8.1f} GB/s ({100 * r['hbm_frac']:5.1f}%)  {r['TFLOPs']:7.1f} TF/s "
                   f"({100 * r['mfma_frac']:5.1f}%)", file=sys.stderr, flush=True)

@@ -150,9 +150,9 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace wq_linear_lowrank needs: t = x . L1^T [M, r] fp16,
- * the fp32 partials of its K chunks, and the split-K workspace of
- * wq_linear_workspace_bytes(M, N, K). 0 for invalid sizes (r must be a multiple
- * of 32 up to 256). */
+ * for M > 16 the fp32 partials of the K chunks it is summed over, and the split-K
+ * workspace of wq_linear_workspace_bytes(M, N, K). 0 for invalid sizes (r must be
+ * a multiple of 32 up to 256). */
 size_t wq_linear_lowrank_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 
 /*

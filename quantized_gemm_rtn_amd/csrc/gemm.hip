@@ -333,13 +333,6 @@ gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Buffer resource of a device array of `bytes` bytes: loads through it take a 32-bit
-// byte offset in a vector register plus one in a scalar register, and loads past the
-// end of the array return zeros (the third-dword value gfx9 expects for raw data).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
 constexpr int kBigSS = 128;                // halves per super-step (one group)
 constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 groups x 256 columns
 

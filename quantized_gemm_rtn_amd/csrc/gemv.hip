@@ -273,28 +273,50 @@ __device__ __forceinline__ void reduce_store(f32x4 acc, int wave, int lane, int 
 // Up-projection of a low-rank branch for a wave's NT 16-channel tiles:
 // acc[j] += t . L2^T, rows m0 .. m0 + 15 of t [M][r] in A and the tile's rows of
 // L2 [N][r] in B, 32 of the rank per 16x16x32 MFMA (the same output layout as the
-// weights' MFMAs). Four steps' loads go out before their MFMAs; rows past M or N
-// read the last row and are never stored.
+// weights' MFMAs); rows past M or N read the last row and are never stored.
+//
+// The operands of the first 32 components are loaded into registers at the end of
+// the prologue (LrFirst), so their latency hides behind the main loop instead of
+// following it; there, the test of r no longer waits (its argument is not among
+// those preloaded into registers, and its load has landed by then), and plain loads
+// leave the LDS accesses of the main loop free of waits (a load straight to LDS
+// would make them wait for it).
 template <int NT>
-__device__ __forceinline__ void lowrank_add16(f32x4 (&acc)[NT], const f16* t, const f16* up, int r, int M, int N,
-                                              int m0, int n0, int lane) {
+struct LrFirst {
+  uint4 a, b[NT];
+  __device__ __forceinline__ void load(const f16* t, const f16* up, int r, int M, int N, int m0, int n0, int lane) {
+    const int q = lane & 15, h = lane >> 4;
+    a = *reinterpret_cast<const uint4*>(t + (size_t)min(m0 + q, M - 1) * r + 8 * h);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      b[j] = *reinterpret_cast<const uint4*>(up + (size_t)min(n0 + 16 * j + q, N - 1) * r + 8 * h);
+  }
+};
+
+// the sum itself, by the wave that loaded `first`: components 32 .. r - 1 from
+// global memory, four steps' loads before their MFMAs
+template <int NT>
+__device__ __forceinline__ void lowrank_add16(f32x4 (&acc)[NT], const LrFirst<NT>& first, const f16* t, const f16* up,
+                                              int r, int M, int N, int m0, int n0, int lane) {
   const int q = lane & 15, h = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = mfma_16x16x32(as_f16x8(first.a), as_f16x8(first.b[j]), acc[j]);
   const f16* ta = t + (size_t)min(m0 + q, M - 1) * r + 8 * h;
   const f16* ub[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) ub[j] = up + (size_t)min(n0 + 16 * j + q, N - 1) * r + 8 * h;
-  for (int s = 0; s < r; s += 128) {
+  for (int s = 32; s < r; s += 128) {
     uint4 a[4], b[4][NT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ss = min(s + 32 * u, r - 32);
-      a[u] = *reinterpret_cast<const uint4*>(ta + ss);
+    for (int u = 0; u < 4; ++u)
+      if (s + 32 * u < r) {  // wave-uniform
+        a[u] = *reinterpret_cast<const uint4*>(ta + s + 32 * u);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b[u][j] = *reinterpret_cast<const uint4*>(ub[j] + ss);
-    }
+        for (int j = 0; j < NT; ++j) b[u][j] = *reinterpret_cast<const uint4*>(ub[j] + s + 32 * u);
+      }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (s + 32 * u < r)  // wave-uniform
+      if (s + 32 * u < r)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j] = mfma_16x16x32(as_f16x8(a[u]), as_f16x8(b[u][j]), acc[j]);
   }
@@ -410,6 +432,8 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   for (int i = D0; i < D; ++i) prefetch(i);
   SparseHead<kSparseBatch, KW> sph;
   if constexpr (SP) sph.load(col, val, sp_e0, sp_e1);
+  LrFirst<1> lr_first;
+  if (lr_r > 0 && wave == 0) lr_first.load(lr_t, lr_up, lr_r, M, N, m0, n0, lane);
   __syncthreads();
 
   // ---- main loop over this wave's groups
@@ -520,7 +544,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   // low-rank branch, once per output tile (wave 0, before the waves' sum)
   if (lr_r > 0 && wave == 0) {
     f32x4 a1[1] = {acc};
-    lowrank_add16<1>(a1, lr_t, lr_up, lr_r, M, N, m0, n0, lane);
+    lowrank_add16<1>(a1, lr_first, lr_t, lr_up, lr_r, M, N, m0, n0, lane);
     acc = a1[0];
   }
   reduce_store<KW>(acc, wave, lane, m0, mrows, n, N, y, y_f32);
@@ -603,6 +627,8 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
 #pragma unroll
     for (int j = 0; j < NT; ++j) sph[j].load(col, val, sp_e0[j], sp_e1[j]);
   }
+  LrFirst<NT> lr_first;
+  if (lr_r > 0 && wave == 0) lr_first.load(lr_t, lr_up, lr_r, M, N, m0, n0, lane);
 
   const f16x2* szr = sz + r * (G + 1);
   const uint32_t magic = magic_1024x2();
@@ -697,7 +723,7 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
     }
   }
   // low-rank branch, once per output tile (wave 0, before the waves' sum)
-  if (lr_r > 0 && wave == 0) lowrank_add16<NT>(acc, lr_t, lr_up, lr_r, M, N, m0, n0, lane);
+  if (lr_r > 0 && wave == 0) lowrank_add16<NT>(acc, lr_first, lr_t, lr_up, lr_r, M, N, m0, n0, lane);
   reduce_store_tiles<KW, NT>(acc, wave, lane, m0, mrows, n0 + r, N, y, y_f32);
 }
 

@@ -21,6 +21,13 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const f16x8& a, const f16x8& b, c
 }
 
 __device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Buffer resource of a device array of `bytes` bytes: loads through it take a 32-bit
+// byte offset in a vector register plus one in a scalar register, and loads past the
+// end of the array return zeros (the third-dword value gfx9 expects for raw data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 

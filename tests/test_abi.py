@@ -162,10 +162,14 @@ def test_lowrank_validation(lib, kw, status):
 
 
 def test_lowrank_workspace_and_empty_batch(lib):
-    # t [1, 32] fp16 and the fp32 partials of the 4 K chunks of 1024 channels
-    assert lib.wq_linear_lowrank_workspace_bytes(1, 11008, 4096, 32) >= 64 + 4 * 32 * 4
+    # up to 16 rows: t [M, r] fp16 alone (256-byte aligned), on top of the GEMM's own
+    assert lib.wq_linear_lowrank_workspace_bytes(1, 11008, 4096, 32) == \
+        lib.wq_linear_workspace_bytes(1, 11008, 4096) + 256
+    assert lib.wq_linear_lowrank_workspace_bytes(16, 11008, 4096, 256) == \
+        lib.wq_linear_workspace_bytes(16, 11008, 4096) + 16 * 256 * 2
+    # more rows: t plus the fp32 partials of the down-projection's K chunks
     assert lib.wq_linear_lowrank_workspace_bytes(512, 8192, 28672, 64) >= \
-        lib.wq_linear_workspace_bytes(512, 8192, 28672) + 512 * 64 * 2 + 28 * 512 * 64 * 4
+        lib.wq_linear_workspace_bytes(512, 8192, 28672) + 512 * 64 * 2
     for bad in ((1, 64, 256, 16), (1, 64, 256, 0), (0, 64, 256, 32), (1, 64, 100, 32), (1, 64, 256, 512)):
         assert lib.wq_linear_lowrank_workspace_bytes(*bad) == 0
     # an empty batch launches nothing and needs no workspace
