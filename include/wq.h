@@ -64,7 +64,13 @@ size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k);
  * wq_quantize_rtn - offline dense-and-sparse split plus RTN group quantization.
  *
  *  W        [N, K] float32, the weights (output channel n, input channel k).
- *  group    must be 128 (WQ_ERR_UNSUPPORTED otherwise).
+ *  group    input channels per quantization group: 128, a larger multiple of 128
+ *           that divides K, or -1 for one group per row (the default of the
+ *           group-size option in the SqueezeLLM explainer, section 5.3);
+ *           WQ_ERR_UNSUPPORTED otherwise. The metadata is always written in the
+ *           layout the linear entry points read, one (s, z) per 128 channels: a
+ *           coarser group's (s, z) is repeated in each of its 128-channel slots,
+ *           so the products below take it unchanged (with group = 128).
  *  sparse_k number of entries moved to the sparse fp16 part, 0 <= sparse_k <= N*K.
  *           They are the sparse_k entries of largest |w| (ties: lower flat index
  *           n*K + k first); the SqueezeLLM explainer (section 2.2) keeps such a
@@ -72,7 +78,8 @@ size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k);
  *           a Hessian sensitivity that needs calibration data, here by magnitude.
  *           The dense part is W with those entries set to +0.
  *  codes    [N, K] uint8 out: q = clamp(rint(w / s) + z, 0, 15) for the dense part.
- *  scales   [N, K/128] fp16 out: s = fp16(max(fl32(fl32(max - min) / 15), 2^-14)).
+ *  scales   [N, K/128] fp16 out: s = fp16(max(fl32(fl32(max - min) / 15), 2^-14)),
+ *           max and min over the group.
  *  zeros    [N, K/128] fp16 out: z = clamp(rint(-min / s), 0, 15), an integer.
  *           (All float32 steps are IEEE, correctly rounded, half-to-even.)
  *  row_ptr  [N+1] int32 out, col [sparse_k] int32 out, val [sparse_k] fp16 out:

@@ -102,15 +102,17 @@ def quantize_workspace_bytes(N, K, sparse_k):
 def quantize_rtn(W, sparse_k: int = 0, group: int = GROUP, workspace=None):
     """Dense-and-sparse split and RTN INT4 quantization of ``W`` (float32 [N, K]).
 
-    Returns a dict with ``codes`` uint8 [N, K], ``scales``/``zeros`` float16
-    [N, K/128], and the sparse part ``row_ptr`` int32 [N+1], ``col`` int32
-    [sparse_k], ``val`` float16 [sparse_k]."""
+    ``group``: 128, a larger multiple of 128 dividing K, or -1 (one group per
+    row). Returns a dict with ``codes`` uint8 [N, K], ``scales``/``zeros``
+    float16 [N, K/128] (a coarser group's values repeated in each of its
+    128-channel slots), and the sparse part ``row_ptr`` int32 [N+1], ``col``
+    int32 [sparse_k], ``val`` float16 [sparse_k]."""
     import torch
     lib = load()
     _need(W, torch.float32, "W")
     N, K = W.shape
     dev = W.device
-    G = K // group if group else 0
+    G = K // GROUP  # metadata slots per row, whatever the quantization group
     codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
     scales = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)
     zeros = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)

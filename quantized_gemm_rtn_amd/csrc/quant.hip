@@ -13,35 +13,58 @@
 // -ffp-contract=off; nothing here would contract anyway).
 //
 // The quantizer is HBM-bound (4 B read + 1 B written per weight); one wave owns
-// one group of 128 weights at a time: a 512-byte coalesced load (two floats per
+// one group at a time: per 128 weights a 512-byte coalesced load (two floats per
 // lane), a butterfly min/max across the wave, and a 128-byte store of codes.
+//
+// Coarser groups (a multiple of 128 channels, up to one group per row, which the
+// group-size option in section 5.3 of the SqueezeLLM explainer has as its default)
+// take the
+// min/max over all their 128-channel chunks and then code each chunk; the (s, z) of
+// such a group is written to every 128-channel slot of the [N, K/128] metadata,
+// the layout the linear kernels read, so their products need no change. With 128
+// the weights stay in registers between the two passes; coarser groups reload them
+// (from cache).
 #include "wq_device.h"
 #include "wq_launch.h"
 
 namespace wq {
 
+// COARSE = false: groups of 128 (gc == 1 at compile time)
+template <bool COARSE>
 __global__ void __launch_bounds__(256)
 rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ mask, int64_t N, int64_t K,
-                    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                    int64_t gc_arg, uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                     uint16_t* __restrict__ zeros) {
   const int lane = threadIdx.x & 63;
-  const int64_t G = K / kGroup;
-  const int64_t total = N * G;
+  const int64_t gc = COARSE ? gc_arg : 1;
+  const int64_t G = K / kGroup;  // 128-channel metadata slots per row
+  const int64_t Gq = G / gc;     // quantization groups per row (gc slots each)
+  const int64_t total = N * Gq;
   const int64_t stride = (int64_t)gridDim.x * 4;
-  for (int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); gid < total; gid += stride) {
-    const int64_t n = gid / G;
-    const int64_t g = gid - n * G;
-    const int64_t off = n * K + g * kGroup + 2 * lane;
+  // two weights of a 128-channel chunk; entries moved to the sparse part count as
+  // +0 in the dense part
+  const auto load = [&](int64_t off) {
     float2 v = *reinterpret_cast<const float2*>(W + off);
     if (mask != nullptr) {
-      // entries moved to the sparse part count as +0 in the dense part
       const uint32_t mw = mask[off >> 5];
       const uint32_t b = (uint32_t)(off & 31);
       if ((mw >> b) & 1u) v.x = 0.0f;
       if ((mw >> (b + 1)) & 1u) v.y = 0.0f;
     }
-    float mn = fminf(v.x, v.y);
-    float mx = fmaxf(v.x, v.y);
+    return v;
+  };
+  for (int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); gid < total; gid += stride) {
+    const int64_t n = gid / Gq;
+    const int64_t g0 = (gid - n * Gq) * gc;  // first metadata slot of the group
+    const int64_t off0 = n * K + g0 * kGroup + 2 * lane;
+    const float2 v0 = load(off0);
+    float mn = fminf(v0.x, v0.y);
+    float mx = fmaxf(v0.x, v0.y);
+    for (int64_t c = 1; c < gc; ++c) {
+      const float2 v = load(off0 + c * kGroup);
+      mn = fminf(mn, fminf(v.x, v.y));
+      mx = fmaxf(mx, fmaxf(v.x, v.y));
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       mn = fminf(mn, __shfl_xor(mn, o));
@@ -54,15 +77,19 @@ rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ ma
     float zf = rintf(__fdiv_rn(-mn, s));
     zf = fminf(fmaxf(zf, 0.0f), 15.0f);
     const int zi = (int)zf;  // an integer, so a -0 never reaches the stored fp16
-    float t0 = rintf(__fdiv_rn(v.x, s)) + (float)zi;
-    float t1 = rintf(__fdiv_rn(v.y, s)) + (float)zi;
-    t0 = fminf(fmaxf(t0, 0.0f), 15.0f);
-    t1 = fminf(fmaxf(t1, 0.0f), 15.0f);
-    const uint32_t q0 = (uint32_t)t0, q1 = (uint32_t)t1;
-    *reinterpret_cast<uint16_t*>(codes + off) = (uint16_t)(q0 | (q1 << 8));
-    if (lane == 0) {
-      scales[gid] = __builtin_bit_cast(uint16_t, s16);
-      zeros[gid] = __builtin_bit_cast(uint16_t, (f16)(float)zi);
+    for (int64_t c = 0; c < gc; ++c) {
+      const int64_t off = off0 + c * kGroup;
+      const float2 v = c == 0 ? v0 : load(off);
+      float t0 = rintf(__fdiv_rn(v.x, s)) + (float)zi;
+      float t1 = rintf(__fdiv_rn(v.y, s)) + (float)zi;
+      t0 = fminf(fmaxf(t0, 0.0f), 15.0f);
+      t1 = fminf(fmaxf(t1, 0.0f), 15.0f);
+      const uint32_t q0 = (uint32_t)t0, q1 = (uint32_t)t1;
+      *reinterpret_cast<uint16_t*>(codes + off) = (uint16_t)(q0 | (q1 << 8));
+      if (lane == 0) {
+        scales[n * G + g0 + c] = __builtin_bit_cast(uint16_t, s16);
+        zeros[n * G + g0 + c] = __builtin_bit_cast(uint16_t, (f16)(float)zi);
+      }
     }
   }
 }
@@ -82,12 +109,16 @@ pack_kernel(const uint8_t* __restrict__ codes, int64_t nwords, uint32_t* __restr
 
 static int64_t clamp_blocks(int64_t want) { return want < 1 ? 1 : (want > 65536 ? 65536 : want); }
 
-hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, uint8_t* codes,
-                           uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
-  const int64_t groups = N * (K / kGroup);
+hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group,
+                           uint8_t* codes, uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+  const int64_t groups = N * (K / group);
   const int64_t blocks = clamp_blocks((groups + 3) / 4);
-  hipLaunchKernelGGL(rtn_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
-                     codes, scales, zeros);
+  if (group == kGroup)
+    hipLaunchKernelGGL(rtn_quantize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
+                       (int64_t)1, codes, scales, zeros);
+  else
+    hipLaunchKernelGGL(rtn_quantize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
+                       group / kGroup, codes, scales, zeros);
   return hipGetLastError();
 }
 

@@ -71,8 +71,10 @@ int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!W || !codes || !scales || !zeros) return WQ_ERR_NULL;
   if (sparse_k > 0 && (!row_ptr || !col || !val)) return WQ_ERR_NULL;
-  if (group != kGroup) return WQ_ERR_UNSUPPORTED;
   if (N < 1 || K < kGroup || K % kGroup != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
+  // quantization group: a multiple of 128 that divides K, or -1 for one group per row
+  const int64_t g = group == -1 ? K : group;
+  if (g < kGroup || g % kGroup != 0 || K % g != 0) return WQ_ERR_UNSUPPORTED;
   if (sparse_k < 0 || sparse_k > N * K) return WQ_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2)) return WQ_ERR_ALIGN;
   if ((row_ptr && !aligned(row_ptr, 4)) || (col && !aligned(col, 4)) || (val && !aligned(val, 2)))
@@ -87,10 +89,10 @@ int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t
   if (sparse_k > 0) {
     const wq::SplitWorkspace ws = wq::split_workspace_carve(workspace, N, K);
     e = wq::launch_split(W, N, K, sparse_k, row_ptr, col, val, ws, s);
-    if (e == hipSuccess) e = wq::launch_quantize(W, ws.mask, N, K, codes, scales, zeros, s);
+    if (e == hipSuccess) e = wq::launch_quantize(W, ws.mask, N, K, g, codes, scales, zeros, s);
   } else {
     if (row_ptr) e = wq::launch_fill_zero_i32(row_ptr, N + 1, s);
-    if (e == hipSuccess) e = wq::launch_quantize(W, nullptr, N, K, codes, scales, zeros, s);
+    if (e == hipSuccess) e = wq::launch_quantize(W, nullptr, N, K, g, codes, scales, zeros, s);
   }
   return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
 }

@@ -120,7 +120,10 @@ def quant(lib, W=A, N=8, K=256, group=128, sparse_k=0, codes=A2, scales=A3, zero
 @pytest.mark.parametrize("kw,status", [
     (dict(W=None), -1), (dict(codes=None), -1), (dict(scales=None), -1), (dict(zeros=None), -1),
     (dict(sparse_k=3), -1), (dict(sparse_k=3, row_ptr=A, col=A, val=None), -1),
-    (dict(group=256), -4), (dict(K=200), -2), (dict(N=0), -2), (dict(sparse_k=-1), -2),
+    # quantization groups: a multiple of 128 dividing K, or -1 (per row)
+    (dict(group=64), -4), (dict(group=192), -4), (dict(group=512), -4), (dict(group=0), -4),
+    (dict(group=-2), -4), (dict(K=384, group=256), -4),
+    (dict(K=200), -2), (dict(N=0), -2), (dict(sparse_k=-1), -2),
     (dict(sparse_k=8 * 256 + 1, row_ptr=A, col=A, val=A), -2),
     (dict(W=MIS), -3), (dict(codes=MIS), -3),
     (dict(sparse_k=3, row_ptr=A, col=A, val=A), -6),

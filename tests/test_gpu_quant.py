@@ -82,3 +82,64 @@ def test_quantize_is_deterministic(gpu_lib):
     b = gpu_lib.quantize_rtn(Wd, sparse_k=L["sparse_k"])
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+# ---------------------------------------------------------------- coarser groups
+@pytest.mark.parametrize("seed,N,K,group,sk", [
+    (31, 37, 1024, 256, 0), (32, 37, 1024, 512, 200), (33, 16, 1024, -1, 0),
+    (34, 300, 640, -1, 1500), (35, 5, 384, 384, 0), (36, 64, 3584, 512, 0),
+])
+def test_coarse_groups_bit_exact(gpu_lib, seed, N, K, group, sk):
+    """Groups of 256..K channels (-1: one per row): codes bit-exact against the
+    oracle quantizing with that group, and each group's (s, z) repeated over its
+    128-channel metadata slots."""
+    import torch
+    g = K if group == -1 else group
+    W = workloads.random_weights(seed, N, K)
+    L = oracle.quantize_layer(W, sk, group=g)
+    say(f"[quant coarse] N,K={N},{K} group={group} sparse_k={sk}")
+    out = gpu_lib.quantize_rtn(to_dev(W, torch), sparse_k=sk, group=group)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["codes"].cpu().numpy(), L["q"]), "codes"
+    rep = g // oracle.GROUP
+    assert np.array_equal(f16_bits_host(out["scales"]), np.repeat(L["s"], rep, axis=1).view(np.uint16)), "scales"
+    assert np.array_equal(f16_bits_host(out["zeros"]), np.repeat(L["z"], rep, axis=1).view(np.uint16)), "zeros"
+    assert np.array_equal(out["row_ptr"].cpu().numpy(), L["row_ptr"]), "row_ptr"
+    if sk:
+        assert np.array_equal(out["col"].cpu().numpy(), L["col"]), "col"
+        assert np.array_equal(f16_bits_host(out["val"]), L["val"].view(np.uint16)), "val"
+
+
+def test_per_row_groups_full_decode_layer(gpu_lib):
+    """One group per row on the 7B up-projection layer [11008, 4096]."""
+    import torch
+    W, _, _ = workloads.make(2)
+    L = oracle.quantize_layer(W, 0, group=W.shape[1])
+    out = gpu_lib.quantize_rtn(to_dev(W, torch), group=-1)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["codes"].cpu().numpy(), L["q"]), "codes"
+    assert np.array_equal(f16_bits_host(out["scales"]), np.repeat(L["s"], 32, axis=1).view(np.uint16)), "scales"
+    assert np.array_equal(f16_bits_host(out["zeros"]), np.repeat(L["z"], 32, axis=1).view(np.uint16)), "zeros"
+
+
+@pytest.mark.parametrize("group", [256, -1])
+@pytest.mark.parametrize("M", [1, 8, 100])
+def test_coarse_group_linear_parity(gpu_lib, group, M):
+    """The linear product on coarse-group metadata (GEMV at M = 1, 8, GEMM at
+    100, with a CSR) against the oracle dequantizing with the true group."""
+    import torch
+    N, K, sk = 300, 1024, 600
+    g = K if group == -1 else group
+    W = workloads.random_weights(41 + M, N, K)
+    x = workloads.random_x(42 + M, M, K)
+    L = oracle.quantize_layer(W, sk, group=g)
+    say(f"[coarse linear] group={group} M={M}")
+    out = gpu_lib.quantize_rtn(to_dev(W, torch), sparse_k=sk, group=group)
+    packed = gpu_lib.pack(out["codes"])
+    y = gpu_lib.linear_sparse(to_dev(x, torch), packed, out["scales"], out["zeros"], out["row_ptr"], out["col"],
+                              out["val"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"], group=g)
+    err = oracle.rel_err_inf(y.cpu().numpy(), ref)
+    say(f"    rel err {err:.3e}")
+    assert err <= oracle.TOL, err

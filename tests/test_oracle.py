@@ -124,18 +124,21 @@ def test_group_minimum_gets_code_zero():
                 assert qg[n, g, amin[n, g]] == 0
 
 
-def test_brute_force_exact_rationals():
+@pytest.mark.parametrize("group", [128, 256])
+def test_brute_force_exact_rationals(group):
     """Each code is the nearest grid point in exact arithmetic; the scale is the
-    fp16 nearest to range/15 and the zero-point the nearest integer to -min/s."""
+    fp16 nearest to range/15 and the zero-point the nearest integer to -min/s,
+    with min and max over the group (at 256 channels, one group per row)."""
     W = workloads.random_weights(11, 4, 256, sigma=0.02)
     W[1, 5] *= 20
     W[2, 200] *= -20
     W[3, 0:128] = np.abs(W[3, 0:128])          # an all-positive group (clamped z)
-    q, s, z = oracle.quantize_rtn(W)
+    q, s, z = oracle.quantize_rtn(W, group)
+    assert s.shape == (4, 256 // group)
     near_half = []
     for n in range(W.shape[0]):
-        for g in range(2):
-            grp = [Fraction(float(v)) for v in W[n, 128 * g:128 * g + 128]]
+        for g in range(256 // group):
+            grp = [Fraction(float(v)) for v in W[n, group * g:group * g + group]]
             mn, mx = min(grp), max(grp)
             S = Fraction(float(s[n, g]))
             Z = int(z[n, g])
@@ -151,7 +154,7 @@ def test_brute_force_exact_rationals():
                 errs = [abs(w - (c - Z) * S) for c in range(16)]
                 best = min(errs)
                 winners = {c for c in range(16) if errs[c] == best}
-                qq = int(q[n, 128 * g + k])
+                qq = int(q[n, group * g + k])
                 if qq not in winners:
                     frac = (w / S) - int(w / S)
                     near_half.append((n, g, k, float(frac)))
