@@ -20,7 +20,8 @@ the same way (at least 200 launches and 20 ms, from one timed replay of 20).
 Printed: ONE JSON line with the metric (GB/s, algorithmic bytes), the roofline
 of the dominant kernel, the CPU oracle baseline, and the other workloads
 (batched decode + sparse, prefill, the 70B down-projection M sweep and one GPU's
-shard of it, the decode and prefill layers with a rank-32 low-rank branch), and,
+shard of it, the decode and prefill layers with a rank-32 low-rank branch and as
+act-order layers), and,
 as context, torch's device copy of the same byte count.
 """
 from __future__ import annotations
@@ -45,11 +46,12 @@ MFMA_F16_PEAK_TFS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 ROTATE_BYTES = 1 << 30
 
 
-def alg_bytes(M, N, K, nnz, y_bytes=2, rank=0):
+def alg_bytes(M, N, K, nnz, y_bytes=2, rank=0, act_order=False):
     """Bytes the method must move: packed codes, fp16 scale+zero, CSR, the fp16
-    low-rank factors, x, y."""
+    low-rank factors, the int32 channel permutation of an act-order layer, x, y."""
     csr = (6 * nnz + 4 * (N + 1)) if nnz else 0
-    return N * K // 2 + N * (K // 128) * 4 + csr + 2 * rank * (K + N) + M * K * 2 + M * N * y_bytes
+    perm = 4 * K if act_order else 0
+    return N * K // 2 + N * (K // 128) * 4 + csr + 2 * rank * (K + N) + perm + M * K * 2 + M * N * y_bytes
 
 
 def alg_flops(M, N, K, nnz, rank=0):
@@ -59,13 +61,18 @@ def alg_flops(M, N, K, nnz, rank=0):
 class Layer:
     """A quantized layer on the GPU, produced by the library's own quantizer."""
 
-    def __init__(self, wq, torch, index, M, K=None, rank=0):
+    def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False):
         W, x, cfg = workloads.make(index, M=M, K=K)
         N, K = W.shape
-        self.N, self.K, self.M, self.rank = N, K, M, rank
+        self.N, self.K, self.M, self.rank, self.act_order = N, K, M, rank, act_order
         self.sparse_k = workloads.sparse_k_for(cfg, N, K)
         Wd = torch.from_numpy(W).cuda()
-        q = wq.quantize_rtn(Wd, sparse_k=self.sparse_k)
+        if act_order:
+            self.perm = torch.from_numpy(workloads.channel_permutation(index + 7, K)).cuda()
+            q = wq.quantize_rtn_act_order(Wd, self.perm, sparse_k=self.sparse_k)
+            self.ws_bytes = wq.linear_act_order_workspace_bytes(M, N, K)
+        else:
+            q = wq.quantize_rtn(Wd, sparse_k=self.sparse_k)
         self.packed = wq.pack(q["codes"])
         self.scales, self.zeros = q["scales"], q["zeros"]
         self.row_ptr, self.col, self.val = q["row_ptr"], q["col"], q["val"]
@@ -80,7 +87,7 @@ class Layer:
 
     def sets(self, torch, rotate_bytes):
         """R independent copies of every input/output, R * bytes >= rotate_bytes."""
-        nb = alg_bytes(self.M, self.N, self.K, self.sparse_k, rank=self.rank)
+        nb = alg_bytes(self.M, self.N, self.K, self.sparse_k, rank=self.rank, act_order=self.act_order)
         R = max(1, min(64, math.ceil(rotate_bytes / nb)))
         out = []
         for r in range(R):
@@ -91,12 +98,17 @@ class Layer:
             if self.rank:
                 s.update(L1=self.L1.clone(), L2=self.L2.clone(),
                          ws=torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda"))
+            if self.act_order:
+                s.update(perm=self.perm.clone(), ws=torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda"))
             out.append(s)
         return out
 
 
 def launch(wq, s, kernel="auto"):
-    if "L1" in s:
+    if "perm" in s:
+        wq.linear_act_order(s["x"], s["perm"], s["packed"], s["scales"], s["zeros"], s["row_ptr"], s["col"],
+                            s["val"], out=s["y"], kernel=kernel, workspace=s["ws"])
+    elif "L1" in s:
         wq.linear_lowrank(s["x"], s["packed"], s["scales"], s["zeros"], s["L1"], s["L2"], s["row_ptr"], s["col"],
                           s["val"], out=s["y"], kernel=kernel, workspace=s["ws"])
     else:
@@ -142,19 +154,21 @@ def replay_length(wq, torch, sets, kernel, min_ms=25.0, min_steps=200, max_steps
     return int(min(max_steps, max(min_steps, math.ceil(min_ms / t))))
 
 
-def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5, rank=0):
+def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5, rank=0, act_order=False):
     """steps = None: enough launches per replay for >= 20 ms (and >= 200 launches);
-    rank > 0: with a low-rank branch of that rank."""
-    L = Layer(wq, torch, index, M, K, rank)
+    rank > 0: with a low-rank branch of that rank; act_order: the layer in a
+    permuted channel order, x gathered through the permutation."""
+    L = Layer(wq, torch, index, M, K, rank, act_order)
     sets = L.sets(torch, ROTATE_BYTES)
     if steps is None:
         steps = replay_length(wq, torch, sets, kernel)
     runs = time_launches(wq, torch, sets, steps, warmup, kernel, repeats=replays)
     ms = float(np.median(runs))
-    nb = alg_bytes(M, L.N, L.K, L.sparse_k, rank=rank)
+    nb = alg_bytes(M, L.N, L.K, L.sparse_k, rank=rank, act_order=act_order)
     nf = alg_flops(M, L.N, L.K, L.sparse_k, rank=rank)
     used = kernel if kernel != "auto" else wq.auto_kernel(M, L.N, L.K)
-    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, rank=rank, kernel=used, steps=steps,
+    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, rank=rank, act_order=act_order, kernel=used,
+               steps=steps,
                us_per_launch=ms * 1e3,
                us_p10=float(np.percentile(runs, 10)) * 1e3, us_p90=float(np.percentile(runs, 90)) * 1e3,
                replays=len(runs),
@@ -308,7 +322,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--replays", type=int, default=5, help="timed replays per workload (median, p10, p90)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel[:K[:rank]]],... "
+    ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel[:K[:rank[:ao]]]],... "
+                    "(ao: an act-order layer) "
                     "(default: the batched-decode, prefill and 70B-sweep set)")
     ap.add_argument("--no-offline", action="store_true", help="skip timing the offline quantizer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -344,24 +359,28 @@ def main():
             for item in args.workloads.split(","):
                 f = item.split(":")
                 plan.append((int(f[0]), int(f[1]), f[2] if len(f) > 2 and f[2] else "auto",
-                             int(f[3]) if len(f) > 3 and f[3] else None, int(f[4]) if len(f) > 4 else 0))
+                             int(f[3]) if len(f) > 3 and f[3] else None, int(f[4]) if len(f) > 4 and f[4] else 0,
+                             len(f) > 5 and f[5] == "ao"))
         else:
-            plan = [(3, 16, "auto", None, 0), (4, 2048, "auto", None, 0), (5, 1, "auto", None, 0),
-                    (5, 8, "auto", None, 0), (5, 64, "auto", None, 0), (5, 512, "auto", None, 0)]
+            plan = [(3, 16, "auto", None, 0, False), (4, 2048, "auto", None, 0, False),
+                    (5, 1, "auto", None, 0, False), (5, 8, "auto", None, 0, False),
+                    (5, 64, "auto", None, 0, False), (5, 512, "auto", None, 0, False)]
             # the other kernel on either side of the crossover
             for M in (8, 64):
                 other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
-                plan.append((5, M, other, None, 0))
+                plan.append((5, M, other, None, 0, False))
             # one GPU's shard of the 70B down-projection split over 8 GPUs along K
             # (K / 8 = 3584 input channels, 28 groups)
-            plan += [(5, 1, "auto", 3584, 0), (5, 512, "auto", 3584, 0)]
-            # the decode and prefill layers with a rank-32 low-rank branch
-            plan += [(2, 1, "auto", None, 32), (4, 2048, "auto", None, 32)]
-        for index, M, kern, Kov, rank in plan:
+            plan += [(5, 1, "auto", 3584, 0, False), (5, 512, "auto", 3584, 0, False)]
+            # the decode and prefill layers with a rank-32 low-rank branch, and as act-order layers
+            plan += [(2, 1, "auto", None, 32, False), (4, 2048, "auto", None, 32, False),
+                     (2, 1, "auto", None, 0, True), (4, 2048, "auto", None, 0, True)]
+        for index, M, kern, Kov, rank, ao in plan:
             r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov, replays=args.replays,
-                        rank=rank)
+                        rank=rank, act_order=ao)
             rows.append(r)
-            print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov}{' r=%d' % rank if rank else ''} "
+            print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov}{' r=%d' % rank if rank else ''}"
+                  f"{' act-order' if ao else ''} "
                   f"{r['kernel']:4s} "
                   f"{r['us_per_launch']:9.2f} us  "
                   f"{r['GBps']:8.1f} GB/s ({100 * r['hbm_frac']:5.1f}%)  {r['TFLOPs']:7.1f} TF/s "

@@ -188,6 +188,50 @@ int wq_linear_lowrank(const uint16_t* x, int64_t M, int64_t K,
                       void* y, int32_t y_dtype, int32_t kernel,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Act-order layers (the GPTQ-R rows, GPTQ with reordering, of the DeepCompressor
+ * README perplexity table): the input channels are quantized in a permuted order,
+ * so a group is a scattered set of original channels (a per-channel group index
+ * g_idx[perm[i]] = i / group). Such a layer is kept in the permuted order: channel
+ * i of its codes, scales, zeros and CSR columns is input channel perm[i].
+ *  perm  [K] int32, 16-byte aligned, a permutation of 0..K-1. Not checked: an
+ *        index outside [0, K) is clamped (wrong values, never an invalid read).
+ */
+
+/* Bytes of device workspace wq_quantize_rtn_act_order needs: W with its columns
+ * permuted (N*K float32, rounded up to 256 bytes) plus wq_quantize_workspace_bytes.
+ * 0 for invalid sizes. */
+size_t wq_quantize_act_order_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k);
+
+/*
+ * wq_quantize_rtn_act_order - wq_quantize_rtn of W[:, perm] (column i of the copy is
+ * column perm[i] of W): the same split, groups, codes, metadata and CSR, all in the
+ * permuted channel order (CSR columns are positions in that order; ties of |w| go
+ * to the lower flat index in that order).
+ *  workspace  required, 256-byte aligned, wq_quantize_act_order_workspace_bytes.
+ */
+int wq_quantize_rtn_act_order(const float* W, int64_t N, int64_t K, int32_t group, const int32_t* perm,
+                              int64_t sparse_k, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                              int32_t* row_ptr, int32_t* col, uint16_t* val, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace wq_linear_act_order needs: x with its columns permuted
+ * (M*K fp16, rounded up to 256 bytes) plus wq_linear_workspace_bytes(M, N, K). */
+size_t wq_linear_act_order_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * wq_linear_act_order - wq_linear_sparse_kernel for a layer in permuted channel
+ * order: y = x[:, perm] . dequant(packed)^T + W_sparse' x[:, perm], which equals
+ * x . W^T for W in the original order. x is in the original channel order; its
+ * columns are gathered through perm into the workspace, then the product runs as
+ * in wq_linear_sparse_kernel (row_ptr may be NULL when nnz == 0).
+ *  workspace  required for M >= 1, 256-byte aligned, wq_linear_act_order_workspace_bytes.
+ */
+int wq_linear_act_order(const uint16_t* x, int64_t M, int64_t K, const int32_t* perm, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                        const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz, void* y,
+                        int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The kernel WQ_KERNEL_AUTO picks for M rows (WQ_KERNEL_GEMV or WQ_KERNEL_GEMM). */
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K);
 

@@ -258,6 +258,52 @@ def linear_rows(x, q, s, z, rows, row_ptr=None, col=None, val=None, group: int =
     return y
 
 
+# Act-order groups: membership by a per-channel group index
+def quantize_rtn_gidx(Wd: np.ndarray, g_idx):
+    """RTN quantization with groups given by a per-channel group index.
+
+    The GPTQ-R rows (GPTQ with reordering) of the DeepCompressor README
+    perplexity table quantize the input channels in a permuted order, so a group
+    is a scattered set of channels: group j = {k : g_idx[k] == j}.  Each group
+    is quantized by the definition of ``quantize_rtn`` (min and max over its
+    members, then the same s, z and codes), which the membership alone decides:
+    the order of the members does not enter.  Returns ``(q uint8 [N,K]`` in the
+    original channel order, ``s, z float16 [N,G])``."""
+    Wd = np.asarray(Wd, dtype=np.float32)
+    g_idx = np.asarray(g_idx)
+    N, K = Wd.shape
+    if g_idx.shape != (K,):
+        raise ValueError("g_idx must have K entries")
+    G = int(g_idx.max()) + 1
+    q = np.empty((N, K), np.uint8)
+    s = np.empty((N, G), np.float16)
+    z = np.empty((N, G), np.float16)
+    for j in range(G):
+        members = np.nonzero(g_idx == j)[0]
+        qj, sj, zj = quantize_rtn(Wd[:, members], group=members.size)  # one group
+        q[:, members] = qj
+        s[:, j] = sj[:, 0]
+        z[:, j] = zj[:, 0]
+    return q, s, z
+
+
+def dequant_gidx(q, s, z, g_idx) -> np.ndarray:
+    """w_hat[n, k] = (q[n, k] - z[n, g_idx[k]]) * s[n, g_idx[k]] in float64."""
+    g_idx = np.asarray(g_idx)
+    S = np.asarray(s).astype(np.float64)[:, g_idx]
+    Z = np.asarray(z).astype(np.float64)[:, g_idx]
+    return (np.asarray(q).astype(np.float64) - Z) * S
+
+
+def linear_ref_gidx(x, q, s, z, g_idx, row_ptr=None, col=None, val=None) -> np.ndarray:
+    """y = x . w_hat^T (+ W_sparse x) in float64 for an act-order layer, all in
+    the original channel order."""
+    y = np.asarray(x).astype(np.float64) @ dequant_gidx(q, s, z, g_idx).T
+    if row_ptr is not None and len(np.asarray(col)):
+        y += sparse_term(x, row_ptr, col, val, np.asarray(q).shape[0])
+    return y
+
+
 def quantize_layer(W: np.ndarray, sparse_k: int = 0, group: int = GROUP):
     """The offline pipeline: split, quantize the dense part, pack."""
     Wd, row_ptr, col, val = split_outliers(W, sparse_k)

@@ -12,6 +12,8 @@ Entry points (the same names as the C ABI, without the ``wq_`` prefix):
 * ``linear_sparse(x, packed, scales, zeros, row_ptr, col, val)``
 * ``linear_lowrank(x, packed, scales, zeros, L1, L2, row_ptr, col, val)``
   the same plus a rank-r fp16 branch (x . L1^T) . L2^T
+* ``quantize_rtn_act_order(W, perm)``, ``linear_act_order(x, perm, ...)``
+  act-order layers, kept in the permuted channel order
 """
 from __future__ import annotations
 
@@ -42,6 +44,12 @@ SIGNATURES = {
     "wq_linear_lowrank_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "wq_linear_lowrank": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
                                          _vp, _vp, _i64, _vp, _i32, _i32, _vp, _sz, _vp]),
+    "wq_quantize_act_order_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "wq_quantize_rtn_act_order": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _vp, _sz, _vp]),
+    "wq_linear_act_order_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "wq_linear_act_order": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
+                                           _vp, _i32, _i32, _vp, _sz, _vp]),
     "wq_auto_kernel": (ctypes.c_int, [_i64, _i64, _i64]),
     "wq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -246,6 +254,88 @@ def linear_lowrank(x, packed, scales, zeros, L1, L2, row_ptr=None, col=None, val
                                nnz, _p(L1), _p(L2), r, _p(out), y_dtype, KERNELS[kernel], _p(workspace), wbytes,
                                _stream(x))
     _check("wq_linear_lowrank", rc)
+    return out
+
+
+def quantize_rtn_act_order(W, perm, sparse_k: int = 0, group: int = GROUP, workspace=None):
+    """``quantize_rtn`` of ``W[:, perm]`` (``perm`` int32 [K], a permutation): the
+    layer of an act-order quantization, kept in the permuted channel order (its
+    CSR columns are positions in that order). Same return value as
+    ``quantize_rtn``."""
+    import torch
+    lib = load()
+    _need(W, torch.float32, "W")
+    _need(perm, torch.int32, "perm")
+    N, K = W.shape
+    if perm.numel() != K:
+        raise ValueError("perm must have K entries")
+    dev = W.device
+    G = K // GROUP
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)
+    zeros = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)
+    row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    col = torch.empty(max(sparse_k, 1), dtype=torch.int32, device=dev)
+    val = torch.empty(max(sparse_k, 1), dtype=torch.float16, device=dev)
+    nbytes = int(lib.wq_quantize_act_order_workspace_bytes(N, K, sparse_k))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    rc = lib.wq_quantize_rtn_act_order(_p(W), N, K, group, _p(perm), sparse_k, _p(codes), _p(scales), _p(zeros),
+                                       _p(row_ptr), _p(col), _p(val), _p(workspace), wbytes, _stream(W))
+    _check("wq_quantize_rtn_act_order", rc)
+    return dict(codes=codes, scales=scales[:, :G], zeros=zeros[:, :G], row_ptr=row_ptr,
+                col=col[:sparse_k], val=val[:sparse_k])
+
+
+def linear_act_order_workspace_bytes(M, N, K):
+    return int(load().wq_linear_act_order_workspace_bytes(M, N, K))
+
+
+def linear_act_order(x, perm, packed, scales, zeros, row_ptr=None, col=None, val=None, out_dtype=None,
+                     kernel: str = "auto", out=None, group: int = GROUP, workspace=None):
+    """y = x . W^T for a layer kept in permuted channel order (``perm`` int32
+    [K]; from ``quantize_rtn_act_order``): x, in the original order, has its
+    columns gathered through ``perm`` and then meets the layer as in
+    ``linear_sparse``."""
+    import torch
+    lib = load()
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    _need(x, torch.float16, "x")
+    _need(perm, torch.int32, "perm")
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.float16, "zeros")
+    M, K = x.shape
+    N = packed.shape[0]
+    if perm.numel() != K or packed.shape[1] * 8 != K or scales.shape != (N, K // group) or \
+            zeros.shape != scales.shape:
+        raise ValueError("inconsistent shapes")
+    nnz = 0
+    if row_ptr is not None:
+        _need(row_ptr, torch.int32, "row_ptr")
+        if row_ptr.numel() != N + 1:
+            raise ValueError("row_ptr must have N+1 entries")
+        nnz = int(col.numel()) if col is not None else 0
+        if nnz:
+            _need(col, torch.int32, "col")
+            _need(val, torch.float16, "val")
+    if out_dtype not in (torch.float16, torch.float32):
+        raise TypeError("out_dtype must be float16 or float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    y_dtype = 1 if out_dtype == torch.float32 else 0
+    if workspace is None:
+        nbytes = int(lib.wq_linear_act_order_workspace_bytes(max(M, 1), N, K))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    rc = lib.wq_linear_act_order(_p(x), M, K, _p(perm), _p(packed), _p(scales), _p(zeros), N, group,
+                                 _p(row_ptr) if row_ptr is not None else None, _p(col) if nnz else None,
+                                 _p(val) if nnz else None, nnz, _p(out), y_dtype, KERNELS[kernel], _p(workspace),
+                                 wbytes, _stream(x))
+    _check("wq_linear_act_order", rc)
     return out
 
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 ARCH = "gfx950"
 
-SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemm.hip", "lowrank.hip"]
+SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemm.hip", "lowrank.hip", "actorder.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -43,6 +43,30 @@ int check_linear_args(const uint16_t* x, int64_t M, int64_t K, const uint32_t* p
   return WQ_OK;
 }
 
+int check_quantize_args(const float* W, int64_t N, int64_t K, int32_t group, int64_t sparse_k, uint8_t* codes,
+                        uint16_t* scales, uint16_t* zeros, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                        void* workspace, size_t workspace_bytes) {
+  if (!W || !codes || !scales || !zeros) return WQ_ERR_NULL;
+  if (sparse_k > 0 && (!row_ptr || !col || !val)) return WQ_ERR_NULL;
+  if (N < 1 || K < kGroup || K % kGroup != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
+  // quantization group: a multiple of 128 that divides K, or -1 for one group per row
+  const int64_t g = group == -1 ? K : group;
+  if (g < kGroup || g % kGroup != 0 || K % g != 0) return WQ_ERR_UNSUPPORTED;
+  if (sparse_k < 0 || sparse_k > N * K) return WQ_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2)) return WQ_ERR_ALIGN;
+  if ((row_ptr && !aligned(row_ptr, 4)) || (col && !aligned(col, 4)) || (val && !aligned(val, 2)))
+    return WQ_ERR_ALIGN;
+  if (sparse_k > 0) {
+    const size_t need = wq::split_workspace_bytes(N, K);
+    if (!workspace || workspace_bytes < need) return WQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
+  }
+  return WQ_OK;
+}
+
+// the permuted copy of W or x at the start of an act-order workspace
+size_t act_order_copy_bytes(int64_t rows, int64_t K, size_t elem) { return ((size_t)rows * K * elem + 255) / 256 * 256; }
+
 }  // namespace
 
 extern "C" {
@@ -69,21 +93,10 @@ size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k) {
 int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t sparse_k, uint8_t* codes,
                     uint16_t* scales, uint16_t* zeros, int32_t* row_ptr, int32_t* col, uint16_t* val,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (!W || !codes || !scales || !zeros) return WQ_ERR_NULL;
-  if (sparse_k > 0 && (!row_ptr || !col || !val)) return WQ_ERR_NULL;
-  if (N < 1 || K < kGroup || K % kGroup != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
-  // quantization group: a multiple of 128 that divides K, or -1 for one group per row
+  const int rc = check_quantize_args(W, N, K, group, sparse_k, codes, scales, zeros, row_ptr, col, val, workspace,
+                                     workspace_bytes);
+  if (rc != WQ_OK) return rc;
   const int64_t g = group == -1 ? K : group;
-  if (g < kGroup || g % kGroup != 0 || K % g != 0) return WQ_ERR_UNSUPPORTED;
-  if (sparse_k < 0 || sparse_k > N * K) return WQ_ERR_SHAPE;
-  if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2)) return WQ_ERR_ALIGN;
-  if ((row_ptr && !aligned(row_ptr, 4)) || (col && !aligned(col, 4)) || (val && !aligned(val, 2)))
-    return WQ_ERR_ALIGN;
-  if (sparse_k > 0) {
-    const size_t need = wq::split_workspace_bytes(N, K);
-    if (!workspace || workspace_bytes < need) return WQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
-  }
   const hipStream_t s = as_stream(stream);
   hipError_t e = hipSuccess;
   if (sparse_k > 0) {
@@ -194,6 +207,59 @@ int wq_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, c
               size_t workspace_bytes, void* stream) {
   return wq_linear_sparse_kernel(x, M, K, packed, scales, zeros, N, group, nullptr, nullptr, nullptr, 0, y,
                                  y_dtype, WQ_KERNEL_AUTO, workspace, workspace_bytes, stream);
+}
+
+size_t wq_quantize_act_order_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k) {
+  if (N < 1 || K < kGroup || K % kGroup != 0 || N >= kMax32 / K) return 0;
+  return act_order_copy_bytes(N, K, 4) + wq_quantize_workspace_bytes(N, K, sparse_k);
+}
+
+int wq_quantize_rtn_act_order(const float* W, int64_t N, int64_t K, int32_t group, const int32_t* perm,
+                              int64_t sparse_k, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                              int32_t* row_ptr, int32_t* col, uint16_t* val, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!perm) return WQ_ERR_NULL;
+  // W's own checks stand in for those of the permuted copy, which lives in the workspace
+  const size_t copy = act_order_copy_bytes(N, K, 4);
+  char* ws = static_cast<char*>(workspace);
+  const size_t inner_bytes = workspace_bytes > copy ? workspace_bytes - copy : 0;
+  int rc = check_quantize_args(W, N, K, group, sparse_k, codes, scales, zeros, row_ptr, col, val,
+                               ws ? ws + copy : nullptr, inner_bytes);
+  if (rc != WQ_OK) return rc;
+  if (!aligned(perm, 16)) return WQ_ERR_ALIGN;
+  if (!ws || workspace_bytes < wq_quantize_act_order_workspace_bytes(N, K, sparse_k)) return WQ_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return WQ_ERR_ALIGN;
+  float* Wp = reinterpret_cast<float*>(ws);
+  if (wq::launch_gather_cols_f32(W, N, K, perm, Wp, as_stream(stream)) != hipSuccess) return WQ_ERR_HIP;
+  return wq_quantize_rtn(Wp, N, K, group, sparse_k, codes, scales, zeros, row_ptr, col, val,
+                         sparse_k > 0 ? ws + copy : nullptr, inner_bytes, stream);
+}
+
+size_t wq_linear_act_order_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) return 0;
+  if (N >= kMax32 / K || M >= kMax32 / K || M >= kMax32 / N) return 0;
+  return act_order_copy_bytes(M, K, 2) + wq::gemm_workspace_bytes(M, N, K);
+}
+
+int wq_linear_act_order(const uint16_t* x, int64_t M, int64_t K, const int32_t* perm, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                        const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz, void* y,
+                        int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!perm) return WQ_ERR_NULL;
+  const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                                   kernel);
+  if (rc != WQ_OK) return rc;
+  if (!aligned(perm, 16)) return WQ_ERR_ALIGN;
+  if (M == 0) return WQ_OK;
+  if (!workspace || workspace_bytes < wq_linear_act_order_workspace_bytes(M, N, K)) return WQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
+  // workspace: x with its columns in the layer's order | the GEMM's split-K workspace
+  char* ws = static_cast<char*>(workspace);
+  const size_t copy = act_order_copy_bytes(M, K, 2);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
+  if (wq::launch_gather_cols_f16(x, M, K, perm, xp, as_stream(stream)) != hipSuccess) return WQ_ERR_HIP;
+  return wq_linear_sparse_kernel(xp, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                                 kernel, ws + copy, workspace_bytes - copy, stream);
 }
 
 }  // extern "C"

@@ -23,6 +23,12 @@ SplitWorkspace split_workspace_carve(void* base, int64_t N, int64_t K);
 hipError_t launch_split(const float* W, int64_t N, int64_t K, int64_t sparse_k, int32_t* row_ptr,
                         int32_t* col, uint16_t* val, const SplitWorkspace& ws, hipStream_t stream);
 hipError_t launch_fill_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
+// dst[r, i] = src[r, perm[i]] for a row-major [rows, K] matrix (K a multiple of 8)
+hipError_t launch_gather_cols_f16(const uint16_t* src, int64_t rows, int64_t K, const int32_t* perm, uint16_t* dst,
+                                  hipStream_t stream);
+hipError_t launch_gather_cols_f32(const float* src, int64_t rows, int64_t K, const int32_t* perm, float* dst,
+                                  hipStream_t stream);
+
 hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group,
                            uint8_t* codes, uint16_t* scales, uint16_t* zeros, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream);

@@ -177,3 +177,48 @@ def test_lowrank_workspace_and_empty_batch(lib):
         assert lib.wq_linear_lowrank_workspace_bytes(*bad) == 0
     # an empty batch launches nothing and needs no workspace
     assert lowrank(lib, M=0, x=None, y=None) == 0
+
+
+# ---------------------------------------------------------------- act-order layers
+def quant_ao(lib, W=A, N=8, K=256, group=128, perm=A5, sparse_k=0, codes=A2, scales=A3, zeros=A4, row_ptr=None,
+             col=None, val=None, ws=A, ws_bytes=1 << 20):
+    return lib.wq_quantize_rtn_act_order(W, N, K, group, perm, sparse_k, codes, scales, zeros, row_ptr, col, val,
+                                         ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(perm=None), -1), (dict(W=None), -1), (dict(group=64), -4), (dict(K=200), -2),
+    (dict(perm=MIS), -3), (dict(ws=None), -6), (dict(ws_bytes=8 * 256 * 4 - 1), -6), (dict(ws=MIS), -3),
+    (dict(sparse_k=3, row_ptr=A, col=A, val=A, ws_bytes=8 * 256 * 4), -6),
+])
+def test_quantize_act_order_validation(lib, kw, status):
+    assert quant_ao(lib, **kw) == status
+
+
+def lin_ao(lib, x=A, M=1, K=256, perm=A5, N=64, group=128, row_ptr=None, nnz=0, y=A2, kernel=0, ws=A,
+           ws_bytes=1 << 20):
+    return lib.wq_linear_act_order(x, M, K, perm, A2, A3, A4, N, group, row_ptr, None, None, nnz, y, 0, kernel, ws,
+                                   ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(perm=None), -1), (dict(x=None), -1), (dict(nnz=3), -1), (dict(group=256), -4), (dict(kernel=7), -4),
+    (dict(K=200), -2), (dict(perm=MIS), -3), (dict(x=MIS), -3),
+    (dict(ws=None), -6), (dict(ws_bytes=255), -6), (dict(ws=MIS), -3),
+])
+def test_linear_act_order_validation(lib, kw, status):
+    assert lin_ao(lib, **kw) == status
+
+
+def test_act_order_workspace_and_empty_batch(lib):
+    # the permuted copy (rounded up to 256 bytes) on top of the plain entry point's workspace
+    assert lib.wq_quantize_act_order_workspace_bytes(8, 256, 0) == 8 * 256 * 4
+    assert lib.wq_quantize_act_order_workspace_bytes(8, 256, 5) == \
+        8 * 256 * 4 + lib.wq_quantize_workspace_bytes(8, 256, 5)
+    assert lib.wq_linear_act_order_workspace_bytes(1, 11008, 4096) == \
+        4096 * 2 + lib.wq_linear_workspace_bytes(1, 11008, 4096)
+    assert lib.wq_linear_act_order_workspace_bytes(3, 64, 128) == 768 + lib.wq_linear_workspace_bytes(3, 64, 128)
+    for bad in ((0, 64, 256), (1, 0, 256), (1, 64, 100)):
+        assert lib.wq_linear_act_order_workspace_bytes(*bad) == 0
+    # an empty batch launches nothing and needs no workspace
+    assert lin_ao(lib, M=0, x=None, y=None, ws=None, ws_bytes=0) == 0

@@ -401,3 +401,62 @@ def test_lowrank_in_the_linear_layer():
     assert np.allclose(ys, full[:, rows], rtol=1e-13, atol=1e-13)
     empty = oracle.lowrank_term(x, np.zeros((0, K), np.float16), np.zeros((N, 0), np.float16))
     assert empty.shape == (M, N) and not empty.any()
+
+
+# ---------------------------------------------------------------- act-order groups
+def _gidx_from_perm(perm, group=128):
+    """Channel perm[i] belongs to group i // group (groups are consecutive in the
+    permuted order)."""
+    g = np.empty(len(perm), np.int64)
+    g[np.asarray(perm)] = np.arange(len(perm)) // group
+    return g
+
+
+@pytest.mark.parametrize("group", [128, 256])
+def test_gidx_contiguous_groups_reduce_to_plain_groups(group):
+    W = workloads.random_weights(81, 7, 512)
+    q, s, z = oracle.quantize_rtn_gidx(W, np.arange(512) // group)
+    q2, s2, z2 = oracle.quantize_rtn(W, group)
+    assert np.array_equal(q, q2) and np.array_equal(s.view(np.uint16), s2.view(np.uint16))
+    assert np.array_equal(z.view(np.uint16), z2.view(np.uint16))
+
+
+def test_gidx_brute_force_exact_rationals():
+    """Scattered groups: each group's scale, zero-point and codes follow from the
+    min and max over its members, in exact arithmetic."""
+    W = workloads.random_weights(82, 3, 256, sigma=0.02)
+    W[1, 7] *= 25
+    perm = workloads.channel_permutation(83, 256)
+    g_idx = _gidx_from_perm(perm)
+    q, s, z = oracle.quantize_rtn_gidx(W, g_idx)
+    for n in range(3):
+        for j in range(2):
+            members = [k for k in range(256) if g_idx[k] == j]
+            assert len(members) == 128 and members != list(range(128 * j, 128 * j + 128))
+            grp = [Fraction(float(W[n, k])) for k in members]
+            mn, mx = min(grp), max(grp)
+            S, Z = Fraction(float(s[n, j])), int(z[n, j])
+            exact = (mx - mn) / 15
+            ulp = Fraction(2) ** (int(np.floor(np.log2(float(S)))) - 10)
+            assert abs(S - exact) <= ulp / 2 + exact * Fraction(1, 2 ** 22)
+            assert Z == min(15, max(0, round(-mn / S)))
+            for k, w in zip(members, grp):
+                errs = [abs(w - (c - Z) * S) for c in range(16)]
+                assert errs[int(q[n, k])] == min(errs)
+
+
+def test_gidx_product_is_invariant_under_the_channel_permutation():
+    """x . w_hat^T with scattered groups equals the product of the permuted
+    activations with the layer in permuted (contiguous-group) order."""
+    M, N, K = 3, 9, 512
+    W = workloads.random_weights(84, N, K)
+    x = workloads.random_x(85, M, K)
+    perm = workloads.channel_permutation(86, K)
+    g_idx = _gidx_from_perm(perm)
+    q, s, z = oracle.quantize_rtn_gidx(W, g_idx)
+    assert np.array_equal(oracle.dequant_gidx(q, s, z, g_idx)[:, perm], oracle.dequant(q[:, perm], s, z))
+    y = oracle.linear_ref_gidx(x, q, s, z, g_idx)
+    y2 = oracle.linear_ref(x[:, perm], q[:, perm], s, z)
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-12)
+    # and it is not the product with the groups taken as contiguous
+    assert not np.allclose(y, oracle.linear_ref(x, q, s, z), rtol=1e-3)

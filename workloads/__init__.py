@@ -193,3 +193,10 @@ def integer_lowrank_factors(seed: int, r: int, N: int, K: int, nnz_per_row: int 
         L1[j, c] = rng.choice([-1, 1], size=c.size).astype(np.float16)
     L2 = rng.integers(-2, 3, size=(N, r)).astype(np.float16)
     return L1, L2
+
+
+def channel_permutation(seed: int, K: int) -> np.ndarray:
+    """A seeded random permutation of the K input channels (int32), standing in
+    for an act-order channel order: GPTQ-R orders channels by a statistic of
+    calibration data, which these synthetic layers do not have."""
+    return np.random.default_rng(seed).permutation(K).astype(np.int32)
