@@ -304,6 +304,51 @@ def linear_ref_gidx(x, q, s, z, g_idx, row_ptr=None, col=None, val=None) -> np.n
     return y
 
 
+# W4A8 with fp16 outlier channels
+QX = 127
+
+
+def quantize_act_int8(x, outliers):
+    """Per-token INT8 activations with fixed fp16 outlier channels.
+
+    The MixQ news item keeps a few activation channels, the outliers, in high
+    precision (they stay the same channels from one decode step to the next) and
+    quantizes the rest of each token's activations to INT8 by its absolute
+    maximum; the INT8 and the high-precision products are added.  The reading
+    here, per row m of x (fp16 values, arithmetic in float32):
+
+    * ``amax`` = max |x[m, k]| over the channels k not in ``outliers``;
+    * ``s = fl32(amax / 127)``, or 1 when amax is 0;
+    * ``xq[m, k] = clamp(rint(fl32(x[m, k] / s)), -127, 127)`` (half to even),
+      and 0 on the outlier channels;
+    * ``xo[m, j] = x[m, outliers[j]]`` (fp16, unchanged).
+
+    Returns ``(xq int8 [M,K], s float32 [M], xo float16 [M, n_out])``."""
+    x = np.asarray(x, dtype=np.float16)
+    outliers = np.asarray(outliers, dtype=np.int64)
+    M, K = x.shape
+    xf = x.astype(np.float32)
+    keep = np.ones(K, bool)
+    keep[outliers] = False
+    amax = np.abs(xf[:, keep]).max(axis=1) if keep.any() else np.zeros(M, np.float32)
+    s = np.where(amax > 0, amax / np.float32(QX), np.float32(1.0)).astype(np.float32)
+    xq = np.clip(np.rint(xf / s[:, None]), -QX, QX).astype(np.int8)
+    xq[:, ~keep] = 0
+    return xq, s, x[:, outliers].copy()
+
+
+def linear_w4a8_ref(x, q, s, z, outliers, group: int = GROUP) -> np.ndarray:
+    """y = s_x[m] * sum_k xq[m, k] * w_hat[n, k] + sum_j xo[m, j] * w_hat[n, outliers[j]]
+    in float64: the INT8 channels and the fp16 outlier channels, both against the
+    dequantized INT4 weights."""
+    xq, sx, xo = quantize_act_int8(x, outliers)
+    W_hat = dequant(q, s, z, group)
+    y = sx.astype(np.float64)[:, None] * (xq.astype(np.float64) @ W_hat.T)
+    if len(np.asarray(outliers)):
+        y += xo.astype(np.float64) @ W_hat[:, np.asarray(outliers)].T
+    return y
+
+
 def quantize_layer(W: np.ndarray, sparse_k: int = 0, group: int = GROUP):
     """The offline pipeline: split, quantize the dense part, pack."""
     Wd, row_ptr, col, val = split_outliers(W, sparse_k)

@@ -460,3 +460,73 @@ def test_gidx_product_is_invariant_under_the_channel_permutation():
     assert np.allclose(y, y2, rtol=1e-12, atol=1e-12)
     # and it is not the product with the groups taken as contiguous
     assert not np.allclose(y, oracle.linear_ref(x, q, s, z), rtol=1e-3)
+
+
+# ---------------------------------------------------------------- W4A8 with fp16 outlier channels
+def test_act_int8_exact_grid_values_come_back():
+    """Activations already on the INT8 grid of a power-of-two step, with the
+    amax at 127 steps, quantize to exactly those integers."""
+    rng = np.random.default_rng(91)
+    ints = rng.integers(-127, 128, size=(4, 256))
+    ints[:, 3] = 127
+    x = (ints * 2.0 ** -9).astype(np.float16)
+    xq, s, xo = oracle.quantize_act_int8(x, [])
+    assert np.all(s == np.float32(2.0 ** -9)) and np.array_equal(xq, ints.astype(np.int8)) and xo.shape == (4, 0)
+
+
+def test_act_int8_brute_force_rationals():
+    """Each INT8 value is the integer nearest to x / s (ties to even) for the
+    float32 s = amax / 127 of its row, outliers excluded from the amax."""
+    x = workloads.random_x(92, 3, 128)
+    outliers = [5, 77]
+    x[:, 77] = np.float16(300.0)
+    xq, s, xo = oracle.quantize_act_int8(x, outliers)
+    for m in range(3):
+        amax = max(abs(float(x[m, k])) for k in range(128) if k not in outliers)
+        assert s[m] == np.float32(np.float32(amax) / np.float32(127))
+        S = Fraction(float(s[m]))
+        for k in range(128):
+            if k in outliers:
+                assert xq[m, k] == 0
+                continue
+            t = Fraction(float(x[m, k])) / S
+            lo = t.numerator // t.denominator
+            near = lo if (t - lo < Fraction(1, 2) or (t - lo == Fraction(1, 2) and lo % 2 == 0)) else lo + 1
+            # the float32 quotient may round onto a tie or across it only within 2^-24 relative
+            if abs(t - lo - Fraction(1, 2)) > abs(t) * Fraction(1, 2 ** 22):
+                assert int(xq[m, k]) == max(-127, min(127, near)), (m, k)
+    assert np.array_equal(xo, x[:, outliers])
+
+
+def test_act_int8_outlier_channels_do_not_move_the_scale():
+    x = workloads.random_x(93, 2, 256)
+    a = oracle.quantize_act_int8(x, [10, 200])
+    x2 = x.copy()
+    x2[:, 10] = np.float16(-5000.0)
+    b = oracle.quantize_act_int8(x2, [10, 200])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert b[2][0, 0] == np.float16(-5000.0)
+    # without the exclusion the scale would follow the outlier
+    c = oracle.quantize_act_int8(x2, [200])
+    assert np.all(c[1] > 20 * a[1])
+
+
+def test_w4a8_product_within_the_int8_rounding_bound():
+    """|y_w4a8 - y_w4a16| <= s_x / 2 * sum_k |w_hat| per output (each INT8 value
+    is within half a step of x / s_x), and outlier channels add no error."""
+    M, N, K = 3, 40, 512
+    W = workloads.random_weights(94, N, K)
+    x = workloads.random_x(95, M, K)
+    outliers = [1, 130, 400]
+    x[:, outliers] *= np.float16(30)
+    q, s, z = oracle.quantize_rtn(W)
+    y8 = oracle.linear_w4a8_ref(x, q, s, z, outliers)
+    y16 = oracle.linear_ref(x, q, s, z)
+    _, sx, _ = oracle.quantize_act_int8(x, outliers)
+    W_hat = oracle.dequant(q, s, z)
+    bound = sx.astype(np.float64)[:, None] / 2 * np.abs(W_hat).sum(axis=1)[None, :] * (1 + 1e-6)
+    assert np.all(np.abs(y8 - y16) <= bound)
+    assert np.abs(y8 - y16).max() > 0
+    # with every channel an outlier the product is the W4A16 one
+    y_all = oracle.linear_w4a8_ref(x, q, s, z, list(range(K)))
+    assert np.allclose(y_all, y16, rtol=1e-12, atol=1e-12)
