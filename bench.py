@@ -61,10 +61,13 @@ def alg_flops(M, N, K, nnz, rank=0):
 class Layer:
     """A quantized layer on the GPU, produced by the library's own quantizer."""
 
-    def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False):
+    def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False, w4a8=False):
         W, x, cfg = workloads.make(index, M=M, K=K)
         N, K = W.shape
-        self.N, self.K, self.M, self.rank, self.act_order = N, K, M, rank, act_order
+        self.N, self.K, self.M, self.rank, self.act_order, self.w4a8 = N, K, M, rank, act_order, w4a8
+        if w4a8:
+            self.outliers = torch.from_numpy(workloads.x_outlier_channels(index, M=M, K=K)).cuda()
+            self.ws_bytes = wq.linear_w4a8_workspace_bytes(M, N, K)
         self.sparse_k = workloads.sparse_k_for(cfg, N, K)
         Wd = torch.from_numpy(W).cuda()
         if act_order:
@@ -100,12 +103,17 @@ class Layer:
                          ws=torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda"))
             if self.act_order:
                 s.update(perm=self.perm.clone(), ws=torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda"))
+            if self.w4a8:
+                s.update(outliers=self.outliers.clone(),
+                         ws=torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda"))
             out.append(s)
         return out
 
 
 def launch(wq, s, kernel="auto"):
-    if "perm" in s:
+    if "outliers" in s:
+        wq.linear_w4a8(s["x"], s["outliers"], s["packed"], s["scales"], s["zeros"], out=s["y"], workspace=s["ws"])
+    elif "perm" in s:
         wq.linear_act_order(s["x"], s["perm"], s["packed"], s["scales"], s["zeros"], s["row_ptr"], s["col"],
                             s["val"], out=s["y"], kernel=kernel, workspace=s["ws"])
     elif "L1" in s:
@@ -154,11 +162,16 @@ def replay_length(wq, torch, sets, kernel, min_ms=25.0, min_steps=200, max_steps
     return int(min(max_steps, max(min_steps, math.ceil(min_ms / t))))
 
 
-def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5, rank=0, act_order=False):
+def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5, rank=0, mode=""):
     """steps = None: enough launches per replay for >= 20 ms (and >= 200 launches);
-    rank > 0: with a low-rank branch of that rank; act_order: the layer in a
-    permuted channel order, x gathered through the permutation."""
-    L = Layer(wq, torch, index, M, K, rank, act_order)
+    rank > 0: with a low-rank branch of that rank; mode "ao": the layer in a
+    permuted channel order, x gathered through the permutation; mode "w8": the
+    W4A8 product with the configuration's activation outlier channels in fp16
+    (the layer has no CSR then)."""
+    act_order, w4a8 = mode == "ao", mode == "w8"
+    L = Layer(wq, torch, index, M, K, rank, act_order, w4a8)
+    if w4a8:
+        L.sparse_k = 0
     sets = L.sets(torch, ROTATE_BYTES)
     if steps is None:
         steps = replay_length(wq, torch, sets, kernel)
@@ -167,7 +180,9 @@ def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5
     nb = alg_bytes(M, L.N, L.K, L.sparse_k, rank=rank, act_order=act_order)
     nf = alg_flops(M, L.N, L.K, L.sparse_k, rank=rank)
     used = kernel if kernel != "auto" else wq.auto_kernel(M, L.N, L.K)
-    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, rank=rank, act_order=act_order, kernel=used,
+    if w4a8:
+        used = "w4a8"
+    res = dict(config=index, M=M, N=L.N, K=L.K, nnz=L.sparse_k, rank=rank, mode=mode, kernel=used,
                steps=steps,
                us_per_launch=ms * 1e3,
                us_p10=float(np.percentile(runs, 10)) * 1e3, us_p90=float(np.percentile(runs, 90)) * 1e3,
@@ -322,8 +337,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--replays", type=int, default=5, help="timed replays per workload (median, p10, p90)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel[:K[:rank[:ao]]]],... "
-                    "(ao: an act-order layer) "
+    ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel[:K[:rank[:mode]]]],... "
+                    "(mode ao: an act-order layer; w8: the W4A8 product) "
                     "(default: the batched-decode, prefill and 70B-sweep set)")
     ap.add_argument("--no-offline", action="store_true", help="skip timing the offline quantizer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -360,27 +375,29 @@ def main():
                 f = item.split(":")
                 plan.append((int(f[0]), int(f[1]), f[2] if len(f) > 2 and f[2] else "auto",
                              int(f[3]) if len(f) > 3 and f[3] else None, int(f[4]) if len(f) > 4 and f[4] else 0,
-                             len(f) > 5 and f[5] == "ao"))
+                             f[5] if len(f) > 5 else ""))
         else:
-            plan = [(3, 16, "auto", None, 0, False), (4, 2048, "auto", None, 0, False),
-                    (5, 1, "auto", None, 0, False), (5, 8, "auto", None, 0, False),
-                    (5, 64, "auto", None, 0, False), (5, 512, "auto", None, 0, False)]
+            plan = [(3, 16, "auto", None, 0, ""), (4, 2048, "auto", None, 0, ""),
+                    (5, 1, "auto", None, 0, ""), (5, 8, "auto", None, 0, ""),
+                    (5, 64, "auto", None, 0, ""), (5, 512, "auto", None, 0, "")]
             # the other kernel on either side of the crossover
             for M in (8, 64):
                 other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
-                plan.append((5, M, other, None, 0, False))
+                plan.append((5, M, other, None, 0, ""))
             # one GPU's shard of the 70B down-projection split over 8 GPUs along K
             # (K / 8 = 3584 input channels, 28 groups)
-            plan += [(5, 1, "auto", 3584, 0, False), (5, 512, "auto", 3584, 0, False)]
+            plan += [(5, 1, "auto", 3584, 0, ""), (5, 512, "auto", 3584, 0, "")]
             # the decode and prefill layers with a rank-32 low-rank branch, and as act-order layers
-            plan += [(2, 1, "auto", None, 32, False), (4, 2048, "auto", None, 32, False),
-                     (2, 1, "auto", None, 0, True), (4, 2048, "auto", None, 0, True)]
-        for index, M, kern, Kov, rank, ao in plan:
+            plan += [(2, 1, "auto", None, 32, ""), (4, 2048, "auto", None, 32, ""),
+                     (2, 1, "auto", None, 0, "ao"), (4, 2048, "auto", None, 0, "ao")]
+            # the prefill layer as a W4A8 product with its 8 fp16 outlier channels
+            plan += [(4, 2048, "auto", None, 0, "w8")]
+        for index, M, kern, Kov, rank, mode in plan:
             r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov, replays=args.replays,
-                        rank=rank, act_order=ao)
+                        rank=rank, mode=mode)
             rows.append(r)
             print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov}{' r=%d' % rank if rank else ''}"
-                  f"{' act-order' if ao else ''} "
+                  f"{' act-order' if mode == 'ao' else ''}{' w4a8' if mode == 'w8' else ''} "
                   f"{r['kernel']:4s} "
                   f"{r['us_per_launch']:9.2f} us  "
                   f"{r['GBps']:8.1f} GB/s ({100 * r['hbm_frac']:5.1f}%)  {r['TFLOPs']:7.1f} TF/s "

@@ -232,6 +232,47 @@ int wq_linear_act_order(const uint16_t* x, int64_t M, int64_t K, const int32_t* 
                         const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz, void* y,
                         int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * W4A8 with fp16 outlier channels (the MixQ news item: most activation channels
+ * in 8 bits on integer matrix units, a few fixed outlier channels in high
+ * precision, the two products added in registers). The weights are the INT4 g128
+ * layer of the other entry points. Per row m of x, over the channels that are not
+ * outliers:  s_x[m] = fl32(amax / 127) (1 when amax is 0),
+ *            xq[m, k] = clamp(rint(fl32(x[m, k] / s_x[m])), -127, 127),
+ * and  y[m, n] = s_x[m] * sum_k xq[m, k] * w_hat[n, k] + sum_j x[m, o_j] * w_hat[n, o_j],
+ * with w_hat = (q - z) * s. INT8 sums are exact (int32) per group of 128 channels;
+ * the rest is fp32 (the outlier weights w_hat are rounded once to fp16, an MFMA
+ * operand).
+ *  outliers  [n_out] int32 channel indices, distinct, in [0, K) (not checked: an
+ *            index out of range is clamped), 0 <= n_out <= 16 (WQ_ERR_UNSUPPORTED
+ *            otherwise); may be NULL when n_out == 0.
+ */
+
+/*
+ * wq_quantize_act_int8 - the activation step alone.
+ *  xq  [M, K] int8 out, 16-byte aligned, in the order the products read it: in
+ *      each 16 consecutive channels c0..c15 the bytes hold c0, c2, c4, c6, c1, c3,
+ *      c5, c7, c8, c10, c12, c14, c9, c11, c13, c15; 0 on outlier channels.
+ *  sx  [M] float32 out.   xo  [M, 16] fp16 out, 16-byte aligned: x[m, o_j] for
+ *      j < n_out, then zeros.
+ */
+int wq_quantize_act_int8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outliers, int64_t n_out,
+                         int8_t* xq, float* sx, uint16_t* xo, void* stream);
+
+/* Bytes of device workspace wq_linear_w4a8 needs (xq, s_x, the outlier
+ * activations and the outlier weights). 0 for invalid sizes. */
+size_t wq_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * wq_linear_w4a8 - y as above. x [M, K] fp16, packed/scales/zeros as in wq_linear
+ * (group must be 128), y [M, N] fp16 or float32 (y_dtype).
+ *  workspace  required for M >= 1, 256-byte aligned, wq_linear_w4a8_workspace_bytes.
+ * Three launches: the activation step, the outlier weights, the INT8 MFMA product.
+ */
+int wq_linear_w4a8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outliers, int64_t n_out,
+                   const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                   void* y, int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The kernel WQ_KERNEL_AUTO picks for M rows (WQ_KERNEL_GEMV or WQ_KERNEL_GEMM). */
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K);
 

@@ -14,6 +14,8 @@ Entry points (the same names as the C ABI, without the ``wq_`` prefix):
   the same plus a rank-r fp16 branch (x . L1^T) . L2^T
 * ``quantize_rtn_act_order(W, perm)``, ``linear_act_order(x, perm, ...)``
   act-order layers, kept in the permuted channel order
+* ``quantize_act_int8(x, outliers)``, ``linear_w4a8(x, outliers, ...)``
+  INT8 activations with fp16 outlier channels on the same INT4 layer
 """
 from __future__ import annotations
 
@@ -50,6 +52,10 @@ SIGNATURES = {
     "wq_linear_act_order_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "wq_linear_act_order": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
                                            _vp, _i32, _i32, _vp, _sz, _vp]),
+    "wq_quantize_act_int8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "wq_linear_w4a8_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "wq_linear_w4a8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _sz,
+                                      _vp]),
     "wq_auto_kernel": (ctypes.c_int, [_i64, _i64, _i64]),
     "wq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -336,6 +342,61 @@ def linear_act_order(x, perm, packed, scales, zeros, row_ptr=None, col=None, val
                                  _p(val) if nnz else None, nnz, _p(out), y_dtype, KERNELS[kernel], _p(workspace),
                                  wbytes, _stream(x))
     _check("wq_linear_act_order", rc)
+    return out
+
+
+def quantize_act_int8(x, outliers):
+    """Per-row INT8 activations with fp16 outlier channels (``outliers`` int32
+    [n_out], n_out <= 16): returns ``xq`` int8 [M, K] in the products' byte order,
+    ``sx`` float32 [M] and ``xo`` float16 [M, 16]."""
+    import torch
+    lib = load()
+    _need(x, torch.float16, "x")
+    _need(outliers, torch.int32, "outliers")
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    sx = torch.empty(max(M, 1), dtype=torch.float32, device=x.device)
+    xo = torch.empty((max(M, 1), 16), dtype=torch.float16, device=x.device)
+    n_out = outliers.numel()
+    _check("wq_quantize_act_int8", lib.wq_quantize_act_int8(_p(x), M, K, _p(outliers) if n_out else None, n_out,
+                                                            _p(xq), _p(sx), _p(xo), _stream(x)))
+    return xq, sx[:M], xo[:M]
+
+
+def linear_w4a8_workspace_bytes(M, N, K):
+    return int(load().wq_linear_w4a8_workspace_bytes(M, N, K))
+
+
+def linear_w4a8(x, outliers, packed, scales, zeros, out_dtype=None, out=None, group: int = GROUP, workspace=None):
+    """y = W4A8 product with fp16 outlier channels (``outliers`` int32 [n_out],
+    n_out <= 16): the INT8 activations are made per call."""
+    import torch
+    lib = load()
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    _need(x, torch.float16, "x")
+    _need(outliers, torch.int32, "outliers")
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.float16, "zeros")
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 8 != K or scales.shape != (N, K // group) or zeros.shape != scales.shape:
+        raise ValueError("inconsistent shapes")
+    if out_dtype not in (torch.float16, torch.float32):
+        raise TypeError("out_dtype must be float16 or float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, out_dtype, "out")
+    if workspace is None:
+        nbytes = int(lib.wq_linear_w4a8_workspace_bytes(max(M, 1), N, K))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    n_out = outliers.numel()
+    rc = lib.wq_linear_w4a8(_p(x), M, K, _p(outliers) if n_out else None, n_out, _p(packed), _p(scales), _p(zeros),
+                            N, group, _p(out), 1 if out_dtype == torch.float32 else 0, _p(workspace), wbytes,
+                            _stream(x))
+    _check("wq_linear_w4a8", rc)
     return out
 
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 ARCH = "gfx950"
 
-SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemm.hip", "lowrank.hip", "actorder.hip"]
+SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemm.hip", "lowrank.hip", "actorder.hip", "w4a8.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -36,10 +36,10 @@ COMMON = [
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 # The quantizer and split decide integers with float32 arithmetic: no contraction.
-PER_FILE = {"quant.hip": ["-ffp-contract=off"], "split.hip": ["-ffp-contract=off"]}
+PER_FILE = {"quant.hip": ["-ffp-contract=off"], "split.hip": ["-ffp-contract=off"], "w4a8.hip": ["-ffp-contract=off"]}
 # The product kernels must keep everything in registers and LDS: the compiler
 # reports each kernel's per-lane scratch, and any use of it fails the build.
-NO_SCRATCH = {"gemv.hip", "gemm.hip", "lowrank.hip"}
+NO_SCRATCH = {"gemv.hip", "gemm.hip", "lowrank.hip", "w4a8.hip"}
 RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
 
 

@@ -13,6 +13,7 @@ namespace {
 constexpr int64_t kGroup = 128;
 constexpr int64_t kMax32 = (int64_t)1 << 31;  // element counts must stay below 2^31
 constexpr int64_t kMaxRank = 256;             // rank of the low-rank branch: multiples of 32 up to this
+constexpr int64_t kMaxOutliers = 16;          // fp16 outlier channels of the W4A8 product
 
 // t [M][r] fp16 of the low-rank branch, at the start of its workspace
 size_t lowrank_t_bytes(int64_t M, int64_t r) { return ((size_t)M * r * 2 + 255) / 256 * 256; }
@@ -233,6 +234,43 @@ int wq_quantize_rtn_act_order(const float* W, int64_t N, int64_t K, int32_t grou
   if (wq::launch_gather_cols_f32(W, N, K, perm, Wp, as_stream(stream)) != hipSuccess) return WQ_ERR_HIP;
   return wq_quantize_rtn(Wp, N, K, group, sparse_k, codes, scales, zeros, row_ptr, col, val,
                          sparse_k > 0 ? ws + copy : nullptr, inner_bytes, stream);
+}
+
+int wq_quantize_act_int8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outliers, int64_t n_out,
+                         int8_t* xq, float* sx, uint16_t* xo, void* stream) {
+  if (n_out > 0 && !outliers) return WQ_ERR_NULL;
+  if (M != 0 && (!x || !xq || !sx || !xo)) return WQ_ERR_NULL;
+  if (n_out < 0 || n_out > kMaxOutliers) return WQ_ERR_UNSUPPORTED;
+  if (M < 0 || K < kGroup || K % kGroup != 0 || M >= kMax32 / K) return WQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(sx, 4) || !aligned(xo, 16) || !aligned(outliers, 4))
+    return WQ_ERR_ALIGN;
+  if (M == 0) return WQ_OK;
+  return wq::launch_act_int8(x, M, K, outliers, n_out, xq, sx, xo, as_stream(stream)) == hipSuccess ? WQ_OK
+                                                                                                    : WQ_ERR_HIP;
+}
+
+size_t wq_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) return 0;
+  if (N >= kMax32 / K || M >= kMax32 / K || M >= kMax32 / N) return 0;
+  return wq::w4a8_workspace_bytes(M, N, K);
+}
+
+int wq_linear_w4a8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outliers, int64_t n_out,
+                   const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                   void* y, int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_out > 0 && !outliers) return WQ_ERR_NULL;
+  const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, nullptr, nullptr, nullptr, 0, y,
+                                   y_dtype, WQ_KERNEL_AUTO);
+  if (rc != WQ_OK) return rc;
+  if (n_out < 0 || n_out > kMaxOutliers) return WQ_ERR_UNSUPPORTED;
+  if (!aligned(outliers, 4)) return WQ_ERR_ALIGN;
+  if (M == 0) return WQ_OK;
+  if (!workspace || workspace_bytes < wq_linear_w4a8_workspace_bytes(M, N, K)) return WQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
+  return wq::launch_w4a8(x, M, K, outliers, n_out, packed, scales, zeros, N, y, y_dtype == WQ_F32, workspace,
+                         as_stream(stream)) == hipSuccess
+             ? WQ_OK
+             : WQ_ERR_HIP;
 }
 
 size_t wq_linear_act_order_workspace_bytes(int64_t M, int64_t N, int64_t K) {

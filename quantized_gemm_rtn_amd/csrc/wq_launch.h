@@ -29,6 +29,14 @@ hipError_t launch_gather_cols_f16(const uint16_t* src, int64_t rows, int64_t K, 
 hipError_t launch_gather_cols_f32(const float* src, int64_t rows, int64_t K, const int32_t* perm, float* dst,
                                   hipStream_t stream);
 
+// W4A8 with fp16 outlier channels (at most 16): workspace = xq | s_x | xo | w_hat of the outliers
+size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_act_int8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outliers, int64_t n_out,
+                           int8_t* xq, float* sx, uint16_t* xo, hipStream_t stream);
+hipError_t launch_w4a8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outliers, int64_t n_out,
+                       const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, void* y,
+                       int y_f32, void* workspace, hipStream_t stream);
+
 hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group,
                            uint8_t* codes, uint16_t* scales, uint16_t* zeros, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream);

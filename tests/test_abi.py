@@ -222,3 +222,32 @@ def test_act_order_workspace_and_empty_batch(lib):
         assert lib.wq_linear_act_order_workspace_bytes(*bad) == 0
     # an empty batch launches nothing and needs no workspace
     assert lin_ao(lib, M=0, x=None, y=None, ws=None, ws_bytes=0) == 0
+
+
+# ---------------------------------------------------------------- W4A8 with fp16 outlier channels
+def lin_w8(lib, x=A, M=4, K=256, outliers=A5, n_out=8, N=64, group=128, y=A2, y_dtype=0, ws=A, ws_bytes=1 << 20):
+    return lib.wq_linear_w4a8(x, M, K, outliers, n_out, A2, A3, A4, N, group, y, y_dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(outliers=None), -1), (dict(x=None), -1), (dict(y=None), -1), (dict(n_out=17), -4), (dict(n_out=-1), -4),
+    (dict(group=256), -4), (dict(y_dtype=5), -4), (dict(K=200), -2), (dict(N=0), -2), (dict(x=MIS), -3),
+    (dict(outliers=ctypes.c_void_p(0x7F0000400002)), -3), (dict(ws=None), -6), (dict(ws_bytes=100), -6),
+    (dict(ws=MIS), -3),
+])
+def test_linear_w4a8_validation(lib, kw, status):
+    assert lin_w8(lib, **kw) == status
+
+
+def test_w4a8_workspace_act_validation_and_empty_batch(lib):
+    # xq (M*K int8), s_x, the outlier activations and weights, each rounded up to 256 bytes
+    assert lib.wq_linear_w4a8_workspace_bytes(4, 64, 256) == 1024 + 256 + 256 + 64 * 16 * 2
+    assert lib.wq_linear_w4a8_workspace_bytes(0, 64, 256) == 0
+    assert lin_w8(lib, M=0, x=None, y=None, ws=None, ws_bytes=0) == 0
+    assert lin_w8(lib, M=0, x=None, y=None, outliers=None, n_out=0, ws=None, ws_bytes=0) == 0
+    act = lib.wq_quantize_act_int8
+    assert act(A, 4, 256, None, 2, A2, A3, A4, None) == -1
+    assert act(A, 4, 256, A5, 17, A2, A3, A4, None) == -4
+    assert act(A, 4, 200, A5, 2, A2, A3, A4, None) == -2
+    assert act(A, 4, 256, A5, 2, MIS, A3, A4, None) == -3
+    assert act(None, 0, 256, None, 0, None, None, None, None) == 0

@@ -200,3 +200,21 @@ def channel_permutation(seed: int, K: int) -> np.ndarray:
     for an act-order channel order: GPTQ-R orders channels by a statistic of
     calibration data, which these synthetic layers do not have."""
     return np.random.default_rng(seed).permutation(K).astype(np.int32)
+
+
+def x_outlier_channels(index: int, M: int | None = None, N: int | None = None, K: int | None = None) -> np.ndarray:
+    """The activation channels ``make`` multiplies for a configuration (sorted
+    int32; empty when the configuration plants none), from the same draws."""
+    cfg = CONFIGS[index]
+    M = cfg.Ms[0] if M is None else M
+    N = cfg.N if N is None else N
+    K = cfg.K if K is None else K
+    if not cfg.x_outlier_channels:
+        return np.zeros(0, np.int32)
+    if cfg.separate_x_seeds:
+        rng = np.random.default_rng(cfg.seed + M)
+    else:
+        rng = np.random.default_rng(cfg.seed)
+        _draw_weights(rng, cfg, N, K)
+    rng.standard_normal((M, K), dtype=np.float32)
+    return np.sort(rng.choice(K, cfg.x_outlier_channels, replace=False)).astype(np.int32)
