@@ -18,10 +18,12 @@
 //  outlier_weights_kernel: w_hat of the outlier channels, fp16 [N][16] (zeros
 //    past n_out), the B operand of one fp16 MFMA per output tile.
 //  w4a8_gemm_kernel: 128 x 128 output tiles, four waves of 2 x 2 tiles of
-//    32x32x32 INT8 MFMAs. Per group of 128 channels a lane loads 64 contiguous
-//    bytes of xq per row tile and 8 code words per column tile (channels
-//    64 h .. 64 h + 63 of the group for lane half h, so the k positions of A and B
-//    agree lane by lane), subtracts the zero-point from the code bytes
+//    32x32x32 INT8 MFMAs. Per group of 128 channels the block stages the group's
+//    activations and codes in LDS with coalesced loads (the next group's loads in
+//    flight during this group's MFMAs, two LDS buffers); a lane reads 64 bytes of
+//    xq per row tile and 8 code words per column tile (channels 64 h .. 64 h + 63
+//    of the group for lane half h, so the k positions of A and B agree lane by
+//    lane), subtracts the zero-point from the code bytes
 //    ((b | 0x80) - z, then ^ 0x80: no borrow crosses bytes since b + 128 > z), and
 //    sums four MFMAs exactly in int32; the group's sum is scaled by s[n, g] into
 //    fp32. The epilogue multiplies by s_x of the row and adds the outlier product.
@@ -127,6 +129,13 @@ outlier_weights_kernel(const uint32_t* __restrict__ packed, const f16* __restric
   }
 }
 
+// Group tiles in LDS: activations 128 rows x 128 bytes (row stride 144 bytes) and
+// codes 128 columns x 64 bytes (stride 80 bytes), two buffers. The strides put the
+// 16-byte fragment reads of eight consecutive lanes (rows or columns 144 or 80
+// bytes apart) in distinct banks.
+constexpr int kW8AStride = 144, kW8BStride = 80;
+constexpr int kW8ABytes = 128 * kW8AStride, kW8BBytes = 128 * kW8BStride;
+
 // 32x32 fp32 / int32 MFMA results: register r of lane (c, h) (c = lane % 32,
 // h = lane / 32) holds row 8 (r / 4) + 4 h + r % 4, column c.
 __global__ void __launch_bounds__(256)
@@ -134,60 +143,109 @@ w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, co
                  int M, int K, const uint32_t* __restrict__ packed, const f16* __restrict__ scales,
                  const f16* __restrict__ zeros, const f16* __restrict__ wo, int N, void* __restrict__ y,
                  int y_f32) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ __align__(16) char lds[2 * (kW8ABytes + kW8BBytes)];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int c = lane & 31, h = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = blockIdx.y * 128 + wm * 64, n0 = blockIdx.x * 128 + wn * 64;
+  const int mb = blockIdx.y * 128, nb = blockIdx.x * 128;
+  const int m0 = mb + wm * 64, n0 = nb + wn * 64;
   const int G = K >> 7;
-  const int8_t* arow[2];
-  const uint32_t* wrow[2];
+  // staging: thread t copies 16-byte chunk (t + 256 i) & 7 of activation row (t + 256 i) >> 3
+  // (i < 4) and chunk (t + 256 i) & 3 of code column (t + 256 i) >> 2 (i < 2): a wave's
+  // load covers 8 whole rows, or the 64-byte groups of 16 columns. Rows past M and
+  // columns past N reread the last one and are never stored.
+  // (32-bit byte offsets: M K and N K / 2 are below 2^31; chunk i of a thread sits
+  // 32 i rows or 64 i columns after chunk 0 in LDS)
+  uint32_t ag[4], bg[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (t >> 3) + 32 * i;
+    ag[i] = (uint32_t)min(mb + row, M - 1) * (uint32_t)K + 16u * (uint32_t)(t & 7);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cl = (t >> 2) + 64 * i;
+    bg[i] = (uint32_t)min(nb + cl, N - 1) * (uint32_t)(K >> 1) + 16u * (uint32_t)(t & 3);
+  }
+  const int al0 = (t >> 3) * kW8AStride + 16 * (t & 7), bl0 = (t >> 2) * kW8BStride + 16 * (t & 3);
+  const char* xqb = reinterpret_cast<const char*>(xq);
+  const char* pkb = reinterpret_cast<const char*>(packed);
+  // The staged data of the next group (plain scalars: held in arrays captured by a
+  // lambda, the compiler moved them to LDS).
+  uint4 p0, p1, p2, p3, p4, p5;
+#define WQ_W8_FETCH(g, r0, r1, r2, r3, r4, r5)                          \
+  r0 = *reinterpret_cast<const uint4*>(xqb + ag[0] + 128 * (g));        \
+  r1 = *reinterpret_cast<const uint4*>(xqb + ag[1] + 128 * (g));        \
+  r2 = *reinterpret_cast<const uint4*>(xqb + ag[2] + 128 * (g));        \
+  r3 = *reinterpret_cast<const uint4*>(xqb + ag[3] + 128 * (g));        \
+  r4 = *reinterpret_cast<const uint4*>(pkb + bg[0] + 64 * (g));         \
+  r5 = *reinterpret_cast<const uint4*>(pkb + bg[1] + 64 * (g));
+#define WQ_W8_STASH(buf, r0, r1, r2, r3, r4, r5)                        \
+  {                                                                     \
+    char* A_ = lds + (buf) * (kW8ABytes + kW8BBytes);                   \
+    char* B_ = A_ + kW8ABytes;                                          \
+    *reinterpret_cast<uint4*>(A_ + al0) = r0;                           \
+    *reinterpret_cast<uint4*>(A_ + al0 + 32 * kW8AStride) = r1;         \
+    *reinterpret_cast<uint4*>(A_ + al0 + 64 * kW8AStride) = r2;         \
+    *reinterpret_cast<uint4*>(A_ + al0 + 96 * kW8AStride) = r3;         \
+    *reinterpret_cast<uint4*>(B_ + bl0) = r4;                           \
+    *reinterpret_cast<uint4*>(B_ + bl0 + 64 * kW8BStride) = r5;         \
+  }
   int col[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    arow[t] = xq + (size_t)min(m0 + 32 * t + c, M - 1) * K + 64 * h;  // rows past M: never stored
-    col[t] = min(n0 + 32 * t + c, N - 1);                              // columns past N: never stored
-    wrow[t] = packed + (size_t)col[t] * (K >> 3) + 8 * h;
-  }
+  for (int j = 0; j < 2; ++j) col[j] = min(n0 + 32 * j + c, N - 1);
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  // group x's data: LDS buffer x & 1
+  WQ_W8_FETCH(0, p0, p1, p2, p3, p4, p5);
+  WQ_W8_STASH(0, p0, p1, p2, p3, p4, p5);
+  __syncthreads();
   for (int g = 0; g < G; ++g) {
-    i32x4 a[2][4];
-    uint4 w[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[t][s] = *reinterpret_cast<const i32x4*>(arow[t] + 128 * g + 16 * s);
-      w[t][0] = *reinterpret_cast<const uint4*>(wrow[t] + 16 * g);
-      w[t][1] = *reinterpret_cast<const uint4*>(wrow[t] + 16 * g + 4);
+    if (g + 1 < G) {  // in flight during this group's MFMAs
+      WQ_W8_FETCH(g + 1, p0, p1, p2, p3, p4, p5);
     }
     float sc[2];
     uint32_t zz[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sc[t] = (float)scales[(size_t)col[t] * G + g];
-      zz[t] = (uint32_t)(int)(float)zeros[(size_t)col[t] * G + g] * 0x01010101u;
+    for (int j = 0; j < 2; ++j) {
+      sc[j] = (float)scales[(size_t)col[j] * G + g];
+      zz[j] = (uint32_t)(int)(float)zeros[(size_t)col[j] * G + g] * 0x01010101u;
+    }
+    const char* A = lds + (g & 1) * (kW8ABytes + kW8BBytes);
+    const char* B = A + kW8ABytes;
+    // lane (c, h): channels 64 h .. 64 h + 63 of the group, 16 per step
+    uint4 w[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const char* bp = B + (wn * 64 + 32 * j + c) * kW8BStride + 32 * h;
+      w[j][0] = *reinterpret_cast<const uint4*>(bp);
+      w[j][1] = *reinterpret_cast<const uint4*>(bp + 16);
     }
     i32x16 part[2][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      i32x4 b[2];
+      i32x4 a[2], b[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t* wd = reinterpret_cast<const uint32_t*>(&w[t][0]);
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const i32x4*>(A + (wm * 64 + 32 * i + c) * kW8AStride + 64 * h + 16 * s);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t* wd = reinterpret_cast<const uint32_t*>(&w[j][0]);
         const uint32_t w0 = wd[2 * s], w1 = wd[2 * s + 1];
         const uint32_t d[4] = {w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[t][e] = (int)(((d[e] | 0x80808080u) - zz[t]) ^ 0x80808080u);
+        for (int e = 0; e < 4; ++e) b[j][e] = (int)(((d[e] | 0x80808080u) - zz[j]) ^ 0x80808080u);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          part[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][s], b[j], s == 0 ? i32x16{} : part[i][j], 0, 0, 0);
+          part[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], s == 0 ? i32x16{} : part[i][j], 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -195,7 +253,13 @@ w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, co
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] += sc[j] * (float)part[i][j][r];
+    // the other buffer was last read in the previous group, before its barrier
+    // the other buffer was last read in the previous group, before its barrier
+    if (g + 1 < G) WQ_W8_STASH((g + 1) & 1, p0, p1, p2, p3, p4, p5);
+    __syncthreads();
   }
+#undef WQ_W8_FETCH
+#undef WQ_W8_STASH
   // epilogue: s_x of the row, plus the outlier channels' product (one fp16 MFMA)
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
