@@ -42,11 +42,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMaxOutliers = 16;
 
-__device__ __forceinline__ bool is_outlier(int k, const int* o, int n_out) {
-  bool hit = false;
+// bit e set: channel 16 c + e is an outlier (one pass over the list per 16 channels)
+__device__ __forceinline__ uint32_t outlier_bits(int c, const int* o, int n_out) {
+  uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxOutliers; ++j) hit |= (j < n_out) & (o[j] == k);
-  return hit;
+  for (int j = 0; j < kMaxOutliers; ++j) m |= (j < n_out && (o[j] >> 4) == c) ? 1u << (o[j] & 15) : 0u;
+  return m;
 }
 
 __global__ void __launch_bounds__(256)
@@ -68,10 +69,11 @@ act_int8_kernel(const f16* __restrict__ x, int64_t M, int K, const int32_t* __re
       const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * c);
       const uint4 b = *reinterpret_cast<const uint4*>(row + 16 * c + 8);
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const uint32_t om = outlier_bits(c, ol, n_out);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float v = fabsf((float)__builtin_bit_cast(f16, (uint16_t)(w[e >> 1] >> (16 * (e & 1)))));
-        if (!is_outlier(16 * c + e, ol, n_out)) amax = fmaxf(amax, v);
+        if (!((om >> e) & 1u)) amax = fmaxf(amax, v);
       }
     }
 #pragma unroll
@@ -88,12 +90,13 @@ act_int8_kernel(const f16* __restrict__ x, int64_t M, int K, const int32_t* __re
       const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * c);
       const uint4 b = *reinterpret_cast<const uint4*>(row + 16 * c + 8);
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const uint32_t om = outlier_bits(c, ol, n_out);
       int qv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float v = (float)__builtin_bit_cast(f16, (uint16_t)(w[e >> 1] >> (16 * (e & 1))));
         float t = fminf(fmaxf(rintf(__fdiv_rn(v, s)), -127.0f), 127.0f);
-        qv[e] = is_outlier(16 * c + e, ol, n_out) ? 0 : (int)t;
+        qv[e] = ((om >> e) & 1u) ? 0 : (int)t;
       }
       // byte order of the 16 channels: 0,2,4,6, 1,3,5,7, 8,10,12,14, 9,11,13,15
       constexpr int ord[16] = {0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15};
