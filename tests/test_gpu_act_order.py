@@ -105,3 +105,21 @@ def test_act_order_identity_permutation_is_the_plain_product(gpu_lib):
     e = gpu_lib.linear_act_order(x[:0], ident, packed, a["scales"], a["zeros"])
     torch.cuda.synchronize()
     assert tuple(e.shape) == (0, N)
+
+
+@pytest.mark.parametrize("group", [256, -1])
+def test_act_order_with_coarser_groups(gpu_lib, group):
+    """Act-order with groups of 256 or one per row: the quantizer's group option
+    applies to the permuted channels."""
+    import torch
+    N, K = 64, 1024
+    g = K if group == -1 else group
+    W = workloads.random_weights(61, N, K)
+    perm = workloads.channel_permutation(62, K)
+    out = gpu_lib.quantize_rtn_act_order(to_dev(W, torch), to_dev(perm, torch), group=group)
+    torch.cuda.synchronize()
+    q, s, z = oracle.quantize_rtn_gidx(W, _gidx(perm, g))
+    assert np.array_equal(out["codes"].cpu().numpy(), q[:, perm])
+    rep = g // oracle.GROUP
+    assert np.array_equal(f16_bits_host(out["scales"]), np.repeat(s, rep, axis=1).view(np.uint16))
+    assert np.array_equal(f16_bits_host(out["zeros"]), np.repeat(z, rep, axis=1).view(np.uint16))
