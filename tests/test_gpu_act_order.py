@@ -87,9 +87,12 @@ def test_act_order_linear_parity(gpu_lib, M, kernel, sk):
         assert oracle.rel_err_inf(y, oracle.linear_ref_gidx(x, q, s, z, _gidx(perm))) <= oracle.TOL
 
 
-def test_act_order_identity_permutation_is_the_plain_product(gpu_lib):
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_act_order_identity_permutation_is_the_plain_product(gpu_lib, M):
+    """Bit for bit, through the decode kernel's two staging paths (M <= 2: the
+    block stages all of x; M = 3: per wave and group)."""
     import torch
-    M, N, K = 3, 256, 512
+    N, K = 256, 512
     W = workloads.random_weights(51, N, K)
     x = to_dev(workloads.random_x(52, M, K), torch)
     ident = to_dev(np.arange(K, dtype=np.int32), torch)
