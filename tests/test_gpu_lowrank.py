@@ -36,6 +36,8 @@ def _run(wq, torch, L, D, x, L1, L2, kernel, sparse, out_dtype=None):
     (200, 256, 4096, 32, True, "auto"),    # large-M GEMM, split K, sparse term in the slice sum
     (300, 300, 1152, 64, False, "auto"),
     (70, 300, 1024, 32, True, "gemv"),     # decode kernel forced above its range
+    (1100, 130, 2048, 64, True, "auto"),   # tall batch: 64-row down-projection blocks, ragged last block
+    (2100, 64, 1024, 32, False, "auto"),   # tall batch, one component tile
 ])
 def test_lowrank_parity(gpu_lib, M, N, K, r, sparse, kernel):
     import torch
@@ -57,7 +59,7 @@ def test_lowrank_parity(gpu_lib, M, N, K, r, sparse, kernel):
 
 
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
-@pytest.mark.parametrize("M,K", [(1, 1024), (16, 2048), (40, 1024), (200, 4096)])
+@pytest.mark.parametrize("M,K", [(1, 1024), (16, 2048), (40, 1024), (200, 4096), (300, 1024)])
 def test_lowrank_integer_exact_fp32(gpu_lib, kernel, M, K):
     """Integer codes, zero-points, activations, sparse values and factors with
     power-of-two scales: t = x . L1^T holds integers up to 1024 (exact in fp16)
@@ -111,3 +113,18 @@ def test_lowrank_deterministic_and_empty(gpu_lib):
     e = _run(gpu_lib, torch, L, D, np.zeros((0, K), np.float16), L1, L2, "auto", True)
     torch.cuda.synchronize()
     assert tuple(e.shape) == (0, N)
+
+
+def test_lowrank_integer_exact_tall_batch(gpu_lib):
+    """The 64-row down-projection (600 rows x rank 256: 80 tiles) on the integer
+    case: bit-identical fp32 output."""
+    import torch
+    M, N, K, r = 600, 96, 1024, 256
+    x, q, s, z, rp, col, val = workloads.integer_case(M + K, M, N, K, nnz_per_row=5)
+    L1, L2 = workloads.integer_lowrank_factors(M + 3, r, N, K)
+    L = dict(q=q, s=s, z=z, packed=oracle.pack(q), row_ptr=rp, col=col, val=val)
+    D = layer_to_dev(L, torch)
+    say(f"[lowrank exact tall] M={M} r={r}")
+    y = _run(gpu_lib, torch, L, D, x, L1, L2, "auto", True, out_dtype=torch.float32)
+    ref = oracle.linear_ref(x, q, s, z, rp, col, val, L1=L1, L2=L2)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
