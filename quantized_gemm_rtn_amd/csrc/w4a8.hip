@@ -55,7 +55,9 @@ act_int8_kernel(const f16* __restrict__ x, int64_t M, int K, const int32_t* __re
                 int8_t* __restrict__ xq, float* __restrict__ sx, f16* __restrict__ xo) {
   __shared__ float red[4];
   __shared__ int o[kMaxOutliers];
-  if (threadIdx.x < kMaxOutliers) o[threadIdx.x] = (int)threadIdx.x < n_out ? outliers[threadIdx.x] : -1;
+  // indices out of [0, K) are clamped here, once, for the mask and the gather alike
+  if (threadIdx.x < kMaxOutliers)
+    o[threadIdx.x] = (int)threadIdx.x < n_out ? min(max(outliers[threadIdx.x], 0), K - 1) : -1;
   __syncthreads();
   int ol[kMaxOutliers];
 #pragma unroll
@@ -85,7 +87,7 @@ act_int8_kernel(const f16* __restrict__ x, int64_t M, int K, const int32_t* __re
     if (threadIdx.x == 0) sx[m] = s;
     if (threadIdx.x < kMaxOutliers)
       xo[m * kMaxOutliers + threadIdx.x] =
-          (int)threadIdx.x < n_out ? row[min(max(ol[threadIdx.x], 0), K - 1)] : (f16)0.0f;
+          (int)threadIdx.x < n_out ? row[ol[threadIdx.x]] : (f16)0.0f;
     for (int c = threadIdx.x; c < chunks; c += 256) {
       const uint4 a = *reinterpret_cast<const uint4*>(row + 16 * c);
       const uint4 b = *reinterpret_cast<const uint4*>(row + 16 * c + 8);
