@@ -36,7 +36,7 @@ COMMON = [
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 # The quantizer and split decide integers with float32 arithmetic: no contraction.
-PER_FILE = {"quant.hip": ["-ffp-contract=off"], "split.hip": ["-ffp-contract=off"], "w4a8.hip": ["-ffp-contract=off"]}
+PER_FILE = {"quant.hip": ["-ffp-contract=off"], "split.hip": ["-ffp-contract=off"], "w4a8.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # The product kernels must keep everything in registers and LDS: the compiler
 # reports each kernel's per-lane scratch, and any use of it fails the build.
 NO_SCRATCH = {"gemv.hip", "gemm.hip", "lowrank.hip", "w4a8.hip"}
