@@ -95,6 +95,18 @@ int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * wq_quantize_rtn_bits - wq_quantize_rtn with codes of `bits` bits, 2 <= bits <= 4
+ * (WQ_ERR_UNSUPPORTED otherwise): qmax = 2^bits - 1 replaces 15 in the formulas
+ * above (the SqueezeLLM explainer quantizes to 3 or 4 bits). The codes, at most
+ * qmax, are written and packed exactly as 4-bit codes, so every product entry
+ * point takes the layer unchanged (the storage and traffic stay those of INT4).
+ * wq_quantize_rtn is wq_quantize_rtn_bits with bits = 4.
+ */
+int wq_quantize_rtn_bits(const float* W, int64_t N, int64_t K, int32_t group, int32_t bits, int64_t sparse_k,
+                         uint8_t* codes, uint16_t* scales, uint16_t* zeros, int32_t* row_ptr, int32_t* col,
+                         uint16_t* val, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * wq_pack - 4-bit packing (AWQ paper, section 1): eight consecutive codes along K
  * per 32-bit word, code k = 8t + i in bits [4i, 4i + 4) of word t.
  *  codes  [N, K] uint8 in (only the low 4 bits of each byte are used).

@@ -93,8 +93,11 @@ def split_outliers(W: np.ndarray, sparse_k: int):
 # --------------------------------------------------------------------------
 # O2-O5: RTN group quantizer
 # --------------------------------------------------------------------------
-def quantize_rtn(Wd: np.ndarray, group: int = GROUP):
-    """Asymmetric INT4 round-to-nearest quantization, one (s, z) per group.
+def quantize_rtn(Wd: np.ndarray, group: int = GROUP, bits: int = 4):
+    """Asymmetric round-to-nearest quantization to ``bits``-bit codes (INT4 by
+    default; the SqueezeLLM explainer quantizes to 3 or 4 bits, section 1 and the
+    weight-bits option of section 4), one (s, z) per group.  Below, 15 is
+    ``qmax = 2^bits - 1``.
 
     For each row n and group j of ``group`` consecutive input channels:
 
@@ -118,14 +121,15 @@ def quantize_rtn(Wd: np.ndarray, group: int = GROUP):
     mn = Wg.min(axis=2)
     mx = Wg.max(axis=2)
     rng = (mx - mn).astype(np.float32)
-    d = (rng / np.float32(QMAX)).astype(np.float32)
+    qmax = (1 << bits) - 1
+    d = (rng / np.float32(qmax)).astype(np.float32)
     d = np.maximum(d, FP16_MIN_NORMAL)
     s16 = d.astype(np.float16)
     s = s16.astype(np.float32)
     zf = np.rint((-mn) / s).astype(np.float32)
-    z = np.clip(zf, 0, QMAX).astype(np.int32)
+    z = np.clip(zf, 0, qmax).astype(np.int32)
     t = np.rint(Wg / s[:, :, None]).astype(np.float32)
-    q = np.clip(t + z[:, :, None].astype(np.float32), 0, QMAX).astype(np.uint8)
+    q = np.clip(t + z[:, :, None].astype(np.float32), 0, qmax).astype(np.uint8)
     return q.reshape(N, K), s16, z.astype(np.float16)
 
 
@@ -349,10 +353,11 @@ def linear_w4a8_ref(x, q, s, z, outliers, group: int = GROUP) -> np.ndarray:
     return y
 
 
-def quantize_layer(W: np.ndarray, sparse_k: int = 0, group: int = GROUP):
-    """The offline pipeline: split, quantize the dense part, pack."""
+def quantize_layer(W: np.ndarray, sparse_k: int = 0, group: int = GROUP, bits: int = 4):
+    """The offline pipeline: split, quantize the dense part, pack (codes of fewer
+    than 4 bits go into the same 4-bit packing)."""
     Wd, row_ptr, col, val = split_outliers(W, sparse_k)
-    q, s, z = quantize_rtn(Wd, group)
+    q, s, z = quantize_rtn(Wd, group, bits)
     return dict(W_dense=Wd, q=q, s=s, z=z, packed=pack(q), row_ptr=row_ptr, col=col, val=val)
 
 

@@ -36,6 +36,8 @@ _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c
 SIGNATURES = {
     "wq_quantize_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "wq_quantize_rtn": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "wq_quantize_rtn_bits": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _sz, _vp]),
     "wq_pack": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "wq_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "wq_linear": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _sz, _vp]),
@@ -113,11 +115,11 @@ def quantize_workspace_bytes(N, K, sparse_k):
     return int(load().wq_quantize_workspace_bytes(N, K, sparse_k))
 
 
-def quantize_rtn(W, sparse_k: int = 0, group: int = GROUP, workspace=None):
+def quantize_rtn(W, sparse_k: int = 0, group: int = GROUP, workspace=None, bits: int = 4):
     """Dense-and-sparse split and RTN INT4 quantization of ``W`` (float32 [N, K]).
 
     ``group``: 128, a larger multiple of 128 dividing K, or -1 (one group per
-    row). Returns a dict with ``codes`` uint8 [N, K], ``scales``/``zeros``
+    row); ``bits``: 2 to 4 (codes of fewer bits in the same 4-bit packing). Returns a dict with ``codes`` uint8 [N, K], ``scales``/``zeros``
     float16 [N, K/128] (a coarser group's values repeated in each of its
     128-channel slots), and the sparse part ``row_ptr`` int32 [N+1], ``col``
     int32 [sparse_k], ``val`` float16 [sparse_k]."""
@@ -136,9 +138,10 @@ def quantize_rtn(W, sparse_k: int = 0, group: int = GROUP, workspace=None):
     nbytes = int(lib.wq_quantize_workspace_bytes(N, K, sparse_k))
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    rc = lib.wq_quantize_rtn(_p(W), N, K, group, sparse_k, _p(codes), _p(scales), _p(zeros), _p(row_ptr),
-                             _p(col), _p(val), _p(workspace), nbytes if workspace is not None else 0, _stream(W))
-    _check("wq_quantize_rtn", rc)
+    rc = lib.wq_quantize_rtn_bits(_p(W), N, K, group, bits, sparse_k, _p(codes), _p(scales), _p(zeros),
+                                  _p(row_ptr), _p(col), _p(val), _p(workspace),
+                                  nbytes if workspace is not None else 0, _stream(W))
+    _check("wq_quantize_rtn_bits", rc)
     return dict(codes=codes, scales=scales[:, :G], zeros=zeros[:, :G], row_ptr=row_ptr,
                 col=col[:sparse_k], val=val[:sparse_k])
 

@@ -3,8 +3,10 @@
 // Quantizer (asymmetric INT4, one scale and zero-point per 128 input channels;
 // round-to-nearest is the calibration-free baseline of the AWQ paper, section 2,
 // and the LLM Compressor article's FAQ; "W4A16 g128" in the DeepCompressor README
-// perplexity table): per group, mn/mx -> s = fp16(max(fl32(mx - mn) / 15, 2^-14)),
-// z = clamp(rint(-mn / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15).
+// perplexity table): per group, mn/mx -> s = fp16(max(fl32(mx - mn) / qmax, 2^-14)),
+// z = clamp(rint(-mn / s), 0, qmax), q = clamp(rint(w / s) + z, 0, qmax), with
+// qmax = 15 for INT4 codes (7 or 3 for the 3- and 2-bit codes the SqueezeLLM
+// explainer also uses, kept in the same 4-bit packing).
 //
 // The codes are integers decided by float32 arithmetic, so this file must round
 // exactly like the definition: IEEE float32 division correctly rounded
@@ -33,7 +35,7 @@ namespace wq {
 template <bool COARSE>
 __global__ void __launch_bounds__(256)
 rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ mask, int64_t N, int64_t K,
-                    int64_t gc_arg, uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                    int64_t gc_arg, float qmax, uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                     uint16_t* __restrict__ zeros) {
   const int lane = threadIdx.x & 63;
   const int64_t gc = COARSE ? gc_arg : 1;
@@ -70,20 +72,20 @@ rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ ma
       mn = fminf(mn, __shfl_xor(mn, o));
       mx = fmaxf(mx, __shfl_xor(mx, o));
     }
-    float d = __fdiv_rn(mx - mn, 15.0f);
+    float d = __fdiv_rn(mx - mn, qmax);
     d = fmaxf(d, 0x1p-14f);
     const f16 s16 = (f16)d;
     const float s = (float)s16;
     float zf = rintf(__fdiv_rn(-mn, s));
-    zf = fminf(fmaxf(zf, 0.0f), 15.0f);
+    zf = fminf(fmaxf(zf, 0.0f), qmax);
     const int zi = (int)zf;  // an integer, so a -0 never reaches the stored fp16
     for (int64_t c = 0; c < gc; ++c) {
       const int64_t off = off0 + c * kGroup;
       const float2 v = c == 0 ? v0 : load(off);
       float t0 = rintf(__fdiv_rn(v.x, s)) + (float)zi;
       float t1 = rintf(__fdiv_rn(v.y, s)) + (float)zi;
-      t0 = fminf(fmaxf(t0, 0.0f), 15.0f);
-      t1 = fminf(fmaxf(t1, 0.0f), 15.0f);
+      t0 = fminf(fmaxf(t0, 0.0f), qmax);
+      t1 = fminf(fmaxf(t1, 0.0f), qmax);
       const uint32_t q0 = (uint32_t)t0, q1 = (uint32_t)t1;
       *reinterpret_cast<uint16_t*>(codes + off) = (uint16_t)(q0 | (q1 << 8));
       if (lane == 0) {
@@ -109,16 +111,17 @@ pack_kernel(const uint8_t* __restrict__ codes, int64_t nwords, uint32_t* __restr
 
 static int64_t clamp_blocks(int64_t want) { return want < 1 ? 1 : (want > 65536 ? 65536 : want); }
 
-hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group,
+hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group, int bits,
                            uint8_t* codes, uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+  const float qmax = (float)((1 << bits) - 1);
   const int64_t groups = N * (K / group);
   const int64_t blocks = clamp_blocks((groups + 3) / 4);
   if (group == kGroup)
     hipLaunchKernelGGL(rtn_quantize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
-                       (int64_t)1, codes, scales, zeros);
+                       (int64_t)1, qmax, codes, scales, zeros);
   else
     hipLaunchKernelGGL(rtn_quantize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
-                       group / kGroup, codes, scales, zeros);
+                       group / kGroup, qmax, codes, scales, zeros);
   return hipGetLastError();
 }
 

@@ -91,24 +91,32 @@ size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k) {
   return wq::split_workspace_bytes(N, K);
 }
 
-int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t sparse_k, uint8_t* codes,
-                    uint16_t* scales, uint16_t* zeros, int32_t* row_ptr, int32_t* col, uint16_t* val,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+int wq_quantize_rtn_bits(const float* W, int64_t N, int64_t K, int32_t group, int32_t bits, int64_t sparse_k,
+                         uint8_t* codes, uint16_t* scales, uint16_t* zeros, int32_t* row_ptr, int32_t* col,
+                         uint16_t* val, void* workspace, size_t workspace_bytes, void* stream) {
   const int rc = check_quantize_args(W, N, K, group, sparse_k, codes, scales, zeros, row_ptr, col, val, workspace,
                                      workspace_bytes);
   if (rc != WQ_OK) return rc;
+  if (bits < 2 || bits > 4) return WQ_ERR_UNSUPPORTED;
   const int64_t g = group == -1 ? K : group;
   const hipStream_t s = as_stream(stream);
   hipError_t e = hipSuccess;
   if (sparse_k > 0) {
     const wq::SplitWorkspace ws = wq::split_workspace_carve(workspace, N, K);
     e = wq::launch_split(W, N, K, sparse_k, row_ptr, col, val, ws, s);
-    if (e == hipSuccess) e = wq::launch_quantize(W, ws.mask, N, K, g, codes, scales, zeros, s);
+    if (e == hipSuccess) e = wq::launch_quantize(W, ws.mask, N, K, g, bits, codes, scales, zeros, s);
   } else {
     if (row_ptr) e = wq::launch_fill_zero_i32(row_ptr, N + 1, s);
-    if (e == hipSuccess) e = wq::launch_quantize(W, nullptr, N, K, g, codes, scales, zeros, s);
+    if (e == hipSuccess) e = wq::launch_quantize(W, nullptr, N, K, g, bits, codes, scales, zeros, s);
   }
   return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+}
+
+int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t sparse_k, uint8_t* codes,
+                    uint16_t* scales, uint16_t* zeros, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return wq_quantize_rtn_bits(W, N, K, group, 4, sparse_k, codes, scales, zeros, row_ptr, col, val, workspace,
+                              workspace_bytes, stream);
 }
 
 int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* stream) {

@@ -37,7 +37,7 @@ hipError_t launch_w4a8(const uint16_t* x, int64_t M, int64_t K, const int32_t* o
                        const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, void* y,
                        int y_f32, void* workspace, hipStream_t stream);
 
-hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group,
+hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group, int bits,
                            uint8_t* codes, uint16_t* scales, uint16_t* zeros, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream);
 

@@ -251,3 +251,11 @@ def test_w4a8_workspace_act_validation_and_empty_batch(lib):
     assert act(A, 4, 200, A5, 2, A2, A3, A4, None) == -2
     assert act(A, 4, 256, A5, 2, MIS, A3, A4, None) == -3
     assert act(None, 0, 256, None, 0, None, None, None, None) == 0
+
+
+def test_quantize_bits_validation(lib):
+    q = lib.wq_quantize_rtn_bits
+    for bad in (1, 5, 8, 0, -1):
+        assert q(A, 8, 256, 128, bad, 0, A2, A3, A4, None, None, None, None, 0, None) == -4
+    assert q(None, 8, 256, 128, 3, 0, A2, A3, A4, None, None, None, None, 0, None) == -1
+    assert q(A, 8, 200, 128, 3, 0, A2, A3, A4, None, None, None, None, 0, None) == -2

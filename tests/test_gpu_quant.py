@@ -143,3 +143,34 @@ def test_coarse_group_linear_parity(gpu_lib, group, M):
     err = oracle.rel_err_inf(y.cpu().numpy(), ref)
     say(f"    rel err {err:.3e}")
     assert err <= oracle.TOL, err
+
+
+# ---------------------------------------------------------------- fewer bits
+@pytest.mark.parametrize("bits,seed,N,K,group,sk", [(3, 41, 37, 1024, 128, 0), (3, 42, 300, 640, 128, 1500),
+                                                    (2, 43, 64, 512, 128, 0), (3, 44, 16, 1024, -1, 100)])
+def test_fewer_bits_bit_exact_and_product(gpu_lib, bits, seed, N, K, group, sk):
+    """3- and 2-bit codes (in the 4-bit packing) bit-exact against the oracle,
+    and the unchanged products (GEMV and GEMM) on them against the oracle."""
+    import torch
+    g = K if group == -1 else group
+    W = workloads.random_weights(seed, N, K)
+    L = oracle.quantize_layer(W, sk, group=g, bits=bits)
+    say(f"[bits] bits={bits} N,K={N},{K} group={group} sparse_k={sk}")
+    out = gpu_lib.quantize_rtn(to_dev(W, torch), sparse_k=sk, group=group, bits=bits)
+    packed = gpu_lib.pack(out["codes"])
+    torch.cuda.synchronize()
+    assert out["codes"].max().item() <= (1 << bits) - 1
+    assert np.array_equal(out["codes"].cpu().numpy(), L["q"]), "codes"
+    rep = g // oracle.GROUP
+    assert np.array_equal(f16_bits_host(out["scales"]), np.repeat(L["s"], rep, axis=1).view(np.uint16)), "scales"
+    assert np.array_equal(f16_bits_host(out["zeros"]), np.repeat(L["z"], rep, axis=1).view(np.uint16)), "zeros"
+    for M in (1, 100):
+        x = workloads.random_x(seed + M, M, K)
+        args = (out["row_ptr"], out["col"], out["val"]) if sk else (None, None, None)
+        y = gpu_lib.linear_sparse(to_dev(x, torch), packed, out["scales"], out["zeros"], *args,
+                                  out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        rargs = (L["row_ptr"], L["col"], L["val"]) if sk else (None, None, None)
+        ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], *rargs, group=g)
+        err = oracle.rel_err_inf(y.cpu().numpy(), ref)
+        assert err <= oracle.TOL, (M, err)

@@ -124,17 +124,19 @@ def test_group_minimum_gets_code_zero():
                 assert qg[n, g, amin[n, g]] == 0
 
 
-@pytest.mark.parametrize("group", [128, 256])
-def test_brute_force_exact_rationals(group):
+@pytest.mark.parametrize("group,bits", [(128, 4), (256, 4), (128, 3), (256, 3), (128, 2)])
+def test_brute_force_exact_rationals(group, bits):
     """Each code is the nearest grid point in exact arithmetic; the scale is the
-    fp16 nearest to range/15 and the zero-point the nearest integer to -min/s,
-    with min and max over the group (at 256 channels, one group per row)."""
+    fp16 nearest to range/qmax (qmax = 2^bits - 1) and the zero-point the
+    nearest integer to -min/s, with min and max over the group (at 256 channels,
+    one group per row)."""
+    qmax = (1 << bits) - 1
     W = workloads.random_weights(11, 4, 256, sigma=0.02)
     W[1, 5] *= 20
     W[2, 200] *= -20
     W[3, 0:128] = np.abs(W[3, 0:128])          # an all-positive group (clamped z)
-    q, s, z = oracle.quantize_rtn(W, group)
-    assert s.shape == (4, 256 // group)
+    q, s, z = oracle.quantize_rtn(W, group, bits)
+    assert s.shape == (4, 256 // group) and q.max() <= qmax
     near_half = []
     for n in range(W.shape[0]):
         for g in range(256 // group):
@@ -142,18 +144,18 @@ def test_brute_force_exact_rationals(group):
             mn, mx = min(grp), max(grp)
             S = Fraction(float(s[n, g]))
             Z = int(z[n, g])
-            # scale: within half an fp16 ulp of the exact range/15 (plus the
+            # scale: within half an fp16 ulp of the exact range/qmax (plus the
             # float32 rounding of the range and quotient)
-            exact = (mx - mn) / 15
+            exact = (mx - mn) / qmax
             ulp = Fraction(2) ** (int(np.floor(np.log2(float(S)))) - 10)
             assert abs(S - exact) <= ulp / 2 + exact * Fraction(1, 2 ** 22)
             # zero-point: nearest integer to -mn/S, clamped to [0, 15]
-            zc = min(15, max(0, round(-mn / S)))
+            zc = min(qmax, max(0, round(-mn / S)))
             assert Z == zc
             for k, w in enumerate(grp):
-                errs = [abs(w - (c - Z) * S) for c in range(16)]
+                errs = [abs(w - (c - Z) * S) for c in range(qmax + 1)]
                 best = min(errs)
-                winners = {c for c in range(16) if errs[c] == best}
+                winners = {c for c in range(qmax + 1) if errs[c] == best}
                 qq = int(q[n, group * g + k])
                 if qq not in winners:
                     frac = (w / S) - int(w / S)
@@ -530,3 +532,19 @@ def test_w4a8_product_within_the_int8_rounding_bound():
     # with every channel an outlier the product is the W4A16 one
     y_all = oracle.linear_w4a8_ref(x, q, s, z, list(range(K)))
     assert np.allclose(y_all, y16, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_fewer_bits_on_grid_weights_come_back(bits):
+    """Weights on a (bits)-bit grid of a power-of-two step, spanning the full code
+    range, quantize to exactly those codes and dequantize back exactly."""
+    qmax = (1 << bits) - 1
+    rng = np.random.default_rng(96 + bits)
+    N, K = 6, 256
+    codes = rng.integers(0, qmax + 1, size=(N, K))
+    codes[:, 0], codes[:, 1] = 0, qmax
+    z = rng.integers(0, qmax + 1, size=(N, 1))
+    W = ((codes - z) * 2.0 ** -6).astype(np.float32)
+    q, s, zz = oracle.quantize_rtn(W, 128, bits)
+    assert np.array_equal(q, codes.astype(np.uint8)) and np.all(s == np.float16(2.0 ** -6))
+    assert np.array_equal(oracle.dequant(q, s, zz), W.astype(np.float64))
