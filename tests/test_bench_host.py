@@ -24,6 +24,12 @@ def test_algorithmic_units():
     assert bench.alg_bytes(16, 4096, 4096, 75497) - bench.alg_bytes(16, 4096, 4096, 0) == 6 * 75497 + 4 * 4097
     assert bench.alg_flops(2048, 14336, 4096, 0) == 2 * 2048 * 14336 * 4096
     assert bench.alg_flops(8, 8192, 28672, 117440) == 2 * 8 * 8192 * 28672 + 2 * 8 * 117440
+    # a rank-r branch adds its two fp16 factors and 2 M r (K + N) flops; an
+    # act-order layer adds its int32 channel permutation
+    assert bench.alg_bytes(1, N, K, 0, rank=32) - bench.alg_bytes(1, N, K, 0) == 2 * 32 * (K + N)
+    assert bench.alg_flops(2048, 14336, 4096, 0, rank=32) - bench.alg_flops(2048, 14336, 4096, 0) == \
+        2 * 2048 * 32 * (4096 + 14336)
+    assert bench.alg_bytes(1, N, K, 0, act_order=True) - bench.alg_bytes(1, N, K, 0) == 4 * K
 
 
 def test_cpu_baseline_record():
