@@ -13,15 +13,20 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All array pointers are DEVICE pointers owned by the caller. The library
- *    never allocates or frees memory, keeps no state between calls, launches its
- *    kernels on `stream` (a hipStream_t; NULL = the default stream) and never
- *    synchronizes: results are ready when work queued after them on `stream`
- *    runs. Calls that share output or workspace buffers must not overlap.
+ *    never allocates or frees memory, launches its kernels on `stream` (a
+ *    hipStream_t; NULL = the default stream, which must belong to the current
+ *    device) and never synchronizes: results are ready when work queued after
+ *    them on `stream` runs. Calls that share output or workspace buffers must not
+ *    overlap.
+ *  - State: none between calls, except a per-thread copy of the last HIP
+ *    launch error (wq_last_hip_error). Every entry point is reentrant and
+ *    thread-safe.
  *  - fp16 values travel as uint16_t bit patterns. All arrays are row-major and
  *    contiguous.
  *  - Every argument is validated on the host BEFORE any HIP call; a failed
  *    validation returns a negative wq_status and launches nothing. A failed
- *    kernel launch returns WQ_ERR_HIP (hipGetLastError() then holds the cause).
+ *    kernel launch returns WQ_ERR_HIP; the library has already read (and so
+ *    cleared) HIP's own error state, and wq_last_hip_error() returns the cause.
  *  - Preconditions the device does not check: inputs are finite; a group's
  *    range (max - min) is at most 15 * 65504 and every |w| of a sparse entry at
  *    most 65504, so scales and sparse values fit fp16; INT4 codes are <= 15.
@@ -290,6 +295,10 @@ int wq_auto_kernel(int64_t M, int64_t N, int64_t K);
 
 /* A static, NUL-terminated description of a wq_status value. */
 const char* wq_status_string(int status);
+
+/* The hipError_t (as int) of the calling thread's last launch that returned
+ * WQ_ERR_HIP, or 0 (hipSuccess) if there was none. */
+int wq_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,7 @@ SIGNATURES = {
     "wq_linear_w4a8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _sz,
                                       _vp]),
     "wq_auto_kernel": (ctypes.c_int, [_i64, _i64, _i64]),
+    "wq_last_hip_error": (ctypes.c_int, []),
     "wq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -204,6 +205,11 @@ def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, ou
                                      _p(out), y_dtype, KERNELS[kernel], _p(workspace), wbytes, _stream(x))
     _check("wq_linear_sparse_kernel", rc)
     return out
+
+
+def last_hip_error() -> int:
+    """hipError_t of this thread's last launch that failed inside the library (0 if none)."""
+    return int(load().wq_last_hip_error())
 
 
 def linear(x, packed, scales, zeros, out_dtype=None, kernel: str = "auto", out=None, group: int = GROUP,

@@ -839,12 +839,11 @@ template <int BM, int BN, int WGM, int WGN, int MINB, int WS>
 static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
   constexpr size_t lds = 2 * (size_t)BM * kBigSS * sizeof(f16) + kBigSzBytes;
   auto kern = gemm_big_kernel<BM, BN, WGM, WGN, MINB, WS>;
-  static bool attr_done = false;  // setting the same attribute twice is harmless
-  if (!attr_done) {
+  // set on every launch (per device, cheap; no state kept between calls)
+  {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_done = true;
   }
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
@@ -857,12 +856,10 @@ template <int BM, int BN, int WGM, int WGN, bool SPARSE>
 static hipError_t launch_tile(GemmArgs a, hipStream_t stream) {
   constexpr size_t lds = 2 * (size_t)BM * kLdsStride * sizeof(f16);
   auto kern = gemm_kernel<BM, BN, WGM, WGN, SPARSE>;
-  static bool attr_done = false;  // setting the same attribute twice is harmless
-  if (lds > 65536 && !attr_done) {
+  if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_done = true;
   }
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;

@@ -189,9 +189,12 @@ __device__ __forceinline__ float row16_sum_to_last(float v) {
 // writing them, which corrupted an LDS address (wrong results, no fault). An
 // accumulation-register operand here keeps them reserved and puts the MFMA in its
 // accumulation-register form, as in 256-thread blocks. No instruction is emitted.
+// The hazard was seen only in blocks of more than 256 threads, which no decode
+// launch uses: kGemvMaxThreads caps the kernels that rely on this guard.
 __device__ __forceinline__ void hold_accumulator(const f32x4& part, const f32x4& acc) {
   asm volatile("" ::"a"(part), "v"(acc));
 }
+constexpr int kGemvMaxThreads = 256;
 
 // (s, z) of a window of D groups in one load: 16 bytes for D = 8, 8 bytes for D = 4.
 template <int D> struct SzVecOf;
@@ -330,6 +333,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
                 const f16* __restrict__ val, void* __restrict__ y, int y_f32, const f16* __restrict__ lr_t,
                 const f16* __restrict__ lr_up, int lr_r) {
   constexpr int T = 64 * KW;
+  static_assert(T <= kGemvMaxThreads, "MFMA results of larger blocks were clobbered (see hold_accumulator)");
   extern __shared__ __align__(16) char smem[];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -566,6 +570,7 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
                  const f16* __restrict__ val, void* __restrict__ y, int y_f32, const f16* __restrict__ lr_t,
                  const f16* __restrict__ lr_up, int lr_r) {
   constexpr int T = 64 * KW;
+  static_assert(T <= kGemvMaxThreads, "MFMA results of larger blocks were clobbered (see hold_accumulator)");
   constexpr int R = 4 * XL;          // rows staged per group
   constexpr int kRowHalves = 136;    // 128 + 8
   extern __shared__ __align__(16) char smem[];
@@ -732,12 +737,13 @@ template <typename Kern>
 static hipError_t launch_rows(Kern kern, size_t lds, int cols, const uint16_t* x, int64_t M, int64_t K,
                               const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N,
                               const int32_t* row_ptr, const int32_t* col, const uint16_t* val, void* y, int y_f32,
-                              const LowRank& lr, hipStream_t stream, size_t* lds_set) {
-  if (lds > 65536 && lds > *lds_set) {
+                              const LowRank& lr, hipStream_t stream) {
+  // set on every call that needs it (the attribute is per device and cheap to set;
+  // caching it here would be state shared by concurrent callers)
+  if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    *lds_set = lds;
   }
   constexpr int64_t kRowsPerLaunch = 65535 * 16;  // gridDim.y limit
   const size_t ysz = y_f32 ? 4 : 2;
@@ -761,12 +767,11 @@ static hipError_t launch_lds(const uint16_t* x, int64_t M, int64_t K, const uint
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                              const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
                              hipStream_t stream) {
-  static size_t lds_set = 0;
   const int64_t G = K / kGroup, mrows = M < 16 ? M : 16, SR = MR == 1 ? 1 : 4 * ((mrows + 3) / 4);
   const size_t lds = (SZV == kSzInRegs ? 0 : (size_t)16 * (G + 1) * 4) + (size_t)mrows * K * 2 +
                      (size_t)2 * G * SR * 4;
   return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR, SP>, lds, 16, x, M, K, packed, scales, zeros, N,
-                     row_ptr, col, val, y, y_f32, lr, stream, &lds_set);
+                     row_ptr, col, val, y, y_f32, lr, stream);
 }
 
 template <int XL, int NT, int SZV, bool SP>
@@ -774,10 +779,9 @@ static hipError_t launch_ring(const uint16_t* x, int64_t M, int64_t K, const uin
                               const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                               const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
                               hipStream_t stream) {
-  static size_t lds_set = 0;
   const size_t lds = (size_t)NT * 16 * (K / kGroup + 1) * 4 + (size_t)kGemvWaves * 4 * XL * 136 * 2;
   return launch_rows(gemv_ring_kernel<kGemvWaves, kGemvRingDepth, XL, NT, SZV, SP>, lds, 16 * NT, x, M, K, packed,
-                     scales, zeros, N, row_ptr, col, val, y, y_f32, lr, stream, &lds_set);
+                     scales, zeros, N, row_ptr, col, val, y, y_f32, lr, stream);
 }
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,

@@ -22,6 +22,17 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// The HIP error of this thread's last failed launch (hipSuccess if none): a
+// launcher reads and clears HIP's own error state, so the cause is kept here for
+// wq_last_hip_error().
+thread_local hipError_t last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return WQ_OK;
+  last_hip_error = e;
+  return WQ_ERR_HIP;
+}
+
 int check_linear_args(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
                       const uint16_t* zeros, int64_t N, int32_t group, const int32_t* row_ptr,
                       const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int32_t y_dtype,
@@ -72,6 +83,8 @@ size_t act_order_copy_bytes(int64_t rows, int64_t K, size_t elem) { return ((siz
 
 extern "C" {
 
+int wq_last_hip_error(void) { return (int)last_hip_error; }
+
 const char* wq_status_string(int status) {
   switch (status) {
     case WQ_OK: return "ok";
@@ -109,7 +122,7 @@ int wq_quantize_rtn_bits(const float* W, int64_t N, int64_t K, int32_t group, in
     if (row_ptr) e = wq::launch_fill_zero_i32(row_ptr, N + 1, s);
     if (e == hipSuccess) e = wq::launch_quantize(W, nullptr, N, K, g, bits, codes, scales, zeros, s);
   }
-  return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+  return hip_status(e);
 }
 
 int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t sparse_k, uint8_t* codes,
@@ -123,7 +136,7 @@ int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* 
   if (!codes || !packed) return WQ_ERR_NULL;
   if (N < 1 || K < 8 || K % 8 != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
   if (!aligned(codes, 16) || !aligned(packed, 16)) return WQ_ERR_ALIGN;
-  return wq::launch_pack(codes, N, K, packed, as_stream(stream)) == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+  return hip_status(wq::launch_pack(codes, N, K, packed, as_stream(stream)));
 }
 
 size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -158,7 +171,7 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K, const uint3
     e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32,
                         workspace != nullptr && aligned(workspace, 16) ? workspace : nullptr, workspace_bytes,
                         wq::LowRank{}, as_stream(stream));
-  return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+  return hip_status(e);
 }
 
 size_t wq_linear_lowrank_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -193,13 +206,13 @@ int wq_linear_lowrank(const uint16_t* x, int64_t M, int64_t K, const uint32_t* p
   const int32_t* rp = nnz > 0 ? row_ptr : nullptr;  // nnz == 0: no sparse term
   const wq::LowRank lr{t, L2, r};
   hipError_t e = wq::launch_lowrank_down(x, M, K, L1, r, part, t, as_stream(stream));
-  if (e != hipSuccess) return WQ_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e);
   if (kernel == WQ_KERNEL_GEMV)
     e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, lr, as_stream(stream));
   else
     e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32, gws, gws_bytes, lr,
                         as_stream(stream));
-  return e == hipSuccess ? WQ_OK : WQ_ERR_HIP;
+  return hip_status(e);
 }
 
 int wq_linear_sparse(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
@@ -239,7 +252,8 @@ int wq_quantize_rtn_act_order(const float* W, int64_t N, int64_t K, int32_t grou
   if (!ws || workspace_bytes < wq_quantize_act_order_workspace_bytes(N, K, sparse_k)) return WQ_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return WQ_ERR_ALIGN;
   float* Wp = reinterpret_cast<float*>(ws);
-  if (wq::launch_gather_cols_f32(W, N, K, perm, Wp, as_stream(stream)) != hipSuccess) return WQ_ERR_HIP;
+  const hipError_t e = wq::launch_gather_cols_f32(W, N, K, perm, Wp, as_stream(stream));
+  if (e != hipSuccess) return hip_status(e);
   return wq_quantize_rtn(Wp, N, K, group, sparse_k, codes, scales, zeros, row_ptr, col, val,
                          sparse_k > 0 ? ws + copy : nullptr, inner_bytes, stream);
 }
@@ -253,8 +267,7 @@ int wq_quantize_act_int8(const uint16_t* x, int64_t M, int64_t K, const int32_t*
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(sx, 4) || !aligned(xo, 16) || !aligned(outliers, 4))
     return WQ_ERR_ALIGN;
   if (M == 0) return WQ_OK;
-  return wq::launch_act_int8(x, M, K, outliers, n_out, xq, sx, xo, as_stream(stream)) == hipSuccess ? WQ_OK
-                                                                                                    : WQ_ERR_HIP;
+  return hip_status(wq::launch_act_int8(x, M, K, outliers, n_out, xq, sx, xo, as_stream(stream)));
 }
 
 size_t wq_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -275,10 +288,8 @@ int wq_linear_w4a8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outli
   if (M == 0) return WQ_OK;
   if (!workspace || workspace_bytes < wq_linear_w4a8_workspace_bytes(M, N, K)) return WQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
-  return wq::launch_w4a8(x, M, K, outliers, n_out, packed, scales, zeros, N, y, y_dtype == WQ_F32, workspace,
-                         as_stream(stream)) == hipSuccess
-             ? WQ_OK
-             : WQ_ERR_HIP;
+  return hip_status(wq::launch_w4a8(x, M, K, outliers, n_out, packed, scales, zeros, N, y, y_dtype == WQ_F32,
+                                   workspace, as_stream(stream)));
 }
 
 size_t wq_linear_act_order_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -303,7 +314,8 @@ int wq_linear_act_order(const uint16_t* x, int64_t M, int64_t K, const int32_t* 
   char* ws = static_cast<char*>(workspace);
   const size_t copy = act_order_copy_bytes(M, K, 2);
   uint16_t* xp = reinterpret_cast<uint16_t*>(ws);
-  if (wq::launch_gather_cols_f16(x, M, K, perm, xp, as_stream(stream)) != hipSuccess) return WQ_ERR_HIP;
+  const hipError_t e = wq::launch_gather_cols_f16(x, M, K, perm, xp, as_stream(stream));
+  if (e != hipSuccess) return hip_status(e);
   return wq_linear_sparse_kernel(xp, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
                                  kernel, ws + copy, workspace_bytes - copy, stream);
 }

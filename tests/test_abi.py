@@ -259,3 +259,30 @@ def test_quantize_bits_validation(lib):
         assert q(A, 8, 256, 128, bad, 0, A2, A3, A4, None, None, None, None, 0, None) == -4
     assert q(None, 8, 256, 128, 3, 0, A2, A3, A4, None, None, None, None, 0, None) == -1
     assert q(A, 8, 200, 128, 3, 0, A2, A3, A4, None, None, None, None, 0, None) == -2
+
+
+def test_last_hip_error_starts_clear(lib):
+    """No launch has failed in this thread: the recorded HIP error is hipSuccess."""
+    assert lib.wq_last_hip_error() == 0
+    assert wq.last_hip_error() == 0
+
+
+def test_header_error_contract():
+    """The header names the query that returns a failed launch's cause, and does
+    not promise that HIP's own error state still holds it (the launchers read it)."""
+    src = open(HEADER).read()
+    assert "wq_last_hip_error" in src
+    assert "hipGetLastError() then holds" not in src
+    assert "keeps no state between calls" not in src
+
+
+def test_no_function_static_state():
+    """No mutable function-local statics in the library sources: such caches are
+    shared, unsynchronized state between concurrent callers and devices."""
+    import glob
+    bad = []
+    for path in glob.glob(os.path.join(ROOT, "quantized_gemm_rtn_amd", "csrc", "*")):
+        for i, line in enumerate(open(path), 1):
+            if re.match(r"^\s+static\s+(?!constexpr\b|const\b|_assert|inline\b|hipError_t\b)", line):
+                bad.append(f"{os.path.basename(path)}:{i}: {line.strip()}")
+    assert not bad, bad
