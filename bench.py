@@ -142,16 +142,30 @@ def time_launches(wq, torch, sets, steps, warmup, kernel="auto", repeats=5):
     torch.cuda.synchronize()
     per_launch = []
     for _ in range(repeats):
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            torch.cuda.synchronize()
-            start.record(stream)
-            g.replay()
-            end.record(stream)
-        torch.cuda.synchronize()
-        per_launch.append(start.elapsed_time(end) / steps)
+        per_launch.append(timed_replay(torch, g, stream) / steps)
     del g
     return per_launch
+
+
+# Busy-wait of about 100 us at the engine clock, queued ahead of each timed replay.
+PRIME_CYCLES = 200_000
+
+
+def timed_replay(torch, g, stream):
+    """Milliseconds between HIP events recorded on `stream` right before and after
+    one replay of graph `g`, between synchronizations. A short busy-wait kernel is
+    queued first, so that the host has submitted the replay before the GPU reaches
+    the start event: the events then bracket the replayed kernels, not the host's
+    graph submission."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(PRIME_CYCLES)
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
 
 
 def replay_length(wq, torch, sets, kernel, min_ms=25.0, min_steps=200, max_steps=20000):
@@ -216,17 +230,49 @@ def stream_copy(torch, nbytes, steps=100):
             dst.copy_(bufs[i % R])
     g.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    us = start.elapsed_time(end) / steps * 1e3
+    us = timed_replay(torch, g, stream) / steps * 1e3
     del g, bufs, dst
     torch.cuda.empty_cache()
     return {"bytes_read": n * 4, "bytes_written": n * 4, "us_per_launch": us,
             "GBps_read_plus_write": 2 * n * 4 / (us * 1e-6) / 1e9}
+
+
+def stream_read(torch, nbytes, steps=200):
+    """Context for the decode rows: one launch of a plain streaming-read kernel
+    (libwq_probe.so) over nbytes, rotating over >= 1 GiB of sources, timed like the
+    layer (graph replays, median of five)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantized_gemm_rtn_amd", "libwq_probe.so"))
+    lib.wq_probe_stream_read.restype = ctypes.c_int
+    lib.wq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = (nbytes + 15) // 16 * 16
+    R = max(1, min(64, math.ceil(ROTATE_BYTES / nbytes)))
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(R)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def go(i):
+        rc = lib.wq_probe_stream_read(ctypes.c_void_p(bufs[i % R].data_ptr()), nbytes,
+                                      ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"wq_probe_stream_read returned {rc}")
+
+    with torch.cuda.stream(stream):
+        for i in range(R):
+            go(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            go(i)
+    g.replay()
+    torch.cuda.synchronize()
+    runs = [timed_replay(torch, g, stream) / steps for _ in range(5)]
+    us = float(np.median(runs)) * 1e3
+    del g, bufs
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "us_per_launch": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
 def measure_offline(wq, torch, index):
@@ -410,8 +456,14 @@ def main():
 
     context = None
     if not args.quick:
-        context = {"torch_copy_headline_bytes": stream_copy(torch, alg_bytes(1, 11008, 4096, 0)),
+        context = {"stream_read_headline_bytes": stream_read(torch, alg_bytes(1, 11008, 4096, 0)),
+                   "stream_read_70b_m1_bytes": stream_read(torch, alg_bytes(1, 8192, 28672, 117440)),
+                   "torch_copy_headline_bytes": stream_copy(torch, alg_bytes(1, 11008, 4096, 0)),
                    "torch_copy_256MiB": stream_copy(torch, 256 << 20, steps=20)}
+        for k in ("stream_read_headline_bytes", "stream_read_70b_m1_bytes"):
+            c = context[k]
+            print(f"# {k} (context): {c['us_per_launch']:.2f} us  {c['GBps']:.1f} GB/s "
+                  f"({100 * c['hbm_frac']:.1f}%)", file=sys.stderr, flush=True)
         print(f"# torch copy (context): {context['torch_copy_headline_bytes']['GBps_read_plus_write']:.1f} GB/s "
               f"(read + write) at the headline size, "
               f"{context['torch_copy_256MiB']['GBps_read_plus_write']:.1f} GB/s at 256 MiB", file=sys.stderr, flush=True)

@@ -20,6 +20,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwq.so")
+# the benchmark's streaming-read probe (include/wq_probe.h), a library of its own
+PROBE_LIB = os.path.join(HERE, "libwq_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemm.hip", "lowrank.hip", "actorder.hip", "w4a8.hip"]
@@ -83,20 +86,27 @@ def scratch_users(remarks: str) -> dict:
     return bad
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libwq.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", "8"))))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libwq.so and the benchmark's probe library;
+    returns the path of libwq.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, int(os.environ.get("MAX_JOBS", "8"))))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

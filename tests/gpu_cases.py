@@ -56,8 +56,33 @@ def run_linear(wq, xd, D, kernel="auto", out_dtype=None, sparse=True):
     return wq.linear(xd, D["packed"], D["scales"], D["zeros"], out_dtype=out_dtype, kernel=kernel)
 
 
-def sample_rows(N, count, seed):
+def sample_rows(N, count, seed, tile=128):
+    """Output channels to check one by one: at least one in every ``tile``-wide
+    column tile (the narrowest tile any product kernel uses), ``count`` more drawn
+    at random, and the edges."""
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(N, min(count, N), replace=False).tolist())
     rows |= {0, N - 1, min(15, N - 1), min(16, N - 1)}
-    return np.array(sorted(rows))
+    for t0 in range(0, N, tile):
+        rows.add(int(rng.integers(t0, min(N, t0 + tile))))
+    rows = np.array(sorted(rows))
+    assert set((rows // tile).tolist()) == set(range((N + tile - 1) // tile)), "a column tile is not sampled"
+    return rows
+
+
+def rel_err_all_rows(y, N, ref_rows, chunk=1024):
+    """max |y - y_ref| / max |y_ref| over EVERY output channel of y [M, N], with the
+    oracle's reference computed ``chunk`` channels at a time (``ref_rows(rows)``
+    returns float64 [M, len(rows)]), so that memory stays bounded at full size."""
+    ys = y.float().cpu().numpy() if hasattr(y, "cpu") else np.asarray(y, np.float64)
+    assert np.isfinite(ys).all()
+    num = den = 0.0
+    seen = np.zeros(N, bool)
+    for a in range(0, N, chunk):
+        rows = np.arange(a, min(N, a + chunk))
+        ref = ref_rows(rows)
+        num = max(num, float(np.max(np.abs(ys[:, rows] - ref))))
+        den = max(den, float(np.max(np.abs(ref))))
+        seen[rows] = True
+    assert seen.all(), "an output channel was not compared"
+    return num / den if den else num
