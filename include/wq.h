@@ -18,8 +18,10 @@
  *    device) and never synchronizes: results are ready when work queued after
  *    them on `stream` runs. Calls that share output or workspace buffers must not
  *    overlap.
- *  - State: none between calls, except a per-thread copy of the last HIP
- *    launch error (wq_last_hip_error). Every entry point is reentrant and
+ *  - State: none between calls, except (a) each GPU's scratch array of
+ *    wq_linear_sparse_noalloc and its device address, looked up under a mutex on
+ *    the first such call on that GPU, and (b) a per-thread copy of the last HIP
+ *    launch error (wq_last_hip_error). Every other entry point is reentrant and
  *    thread-safe.
  *  - fp16 values travel as uint16_t bit patterns. All arrays are row-major and
  *    contiguous.
@@ -52,8 +54,12 @@ typedef enum {
   WQ_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned                  */
   WQ_ERR_UNSUPPORTED = -4, /* group size other than 128, unknown dtype / kernel */
   WQ_ERR_HIP = -5,         /* a kernel launch failed                            */
-  WQ_ERR_WORKSPACE = -6    /* workspace missing or smaller than required        */
+  WQ_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required        */
+  WQ_ERR_SCRATCH = -7      /* needs more than WQ_NOALLOC_SCRATCH_BYTES          */
 } wq_status;
+
+/* Bytes of the scratch array wq_linear_sparse_noalloc keeps on each GPU. */
+#define WQ_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
 
 typedef enum { WQ_F16 = 0, WQ_F32 = 1 } wq_dtype;
 
@@ -172,6 +178,30 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K,
                             const int32_t* row_ptr, const int32_t* col, const uint16_t* val,
                             int64_t nnz, void* y, int32_t y_dtype, int32_t kernel,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wq_linear_sparse_noalloc - wq_linear_sparse (kernel chosen by M; row_ptr may be
+ * NULL when nnz == 0, the dense product) for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace and allocates nothing: the split-K partial sums
+ * and transposed activations of the GEMM go to a scratch array of
+ * WQ_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory from the
+ * first such call on that GPU (the current device) until the process ends.
+ *  - A product that would need more (wq_linear_workspace_bytes(M, N, K) above
+ *    WQ_NOALLOC_SCRATCH_BYTES on the GEMM path) returns WQ_ERR_SCRATCH and
+ *    launches nothing.
+ *  - Every call on one GPU uses the same scratch: calls that can run at the same
+ *    time on one GPU (other streams, other host threads) race and give wrong
+ *    results. Queue them on one stream, or use wq_linear_sparse with separate
+ *    workspaces. Nothing in the scratch needs to start at zero: each call writes
+ *    what it later reads.
+ *  - Results are identical to wq_linear_sparse given a full workspace.
+ */
+int wq_linear_sparse_noalloc(const uint16_t* x, int64_t M, int64_t K,
+                             const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                             int64_t N, int32_t group,
+                             const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
+                             void* y, int32_t y_dtype, void* stream);
 
 /* Bytes of device workspace wq_linear_lowrank needs: t = x . L1^T [M, r] fp16,
  * for M > 16 the fp32 partials of the K chunks it is summed over, and the split-K

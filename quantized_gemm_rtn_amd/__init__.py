@@ -28,7 +28,7 @@ GROUP = 128
 
 WQ_OK = 0
 STATUS = {0: "WQ_OK", -1: "WQ_ERR_NULL", -2: "WQ_ERR_SHAPE", -3: "WQ_ERR_ALIGN",
-          -4: "WQ_ERR_UNSUPPORTED", -5: "WQ_ERR_HIP", -6: "WQ_ERR_WORKSPACE"}
+          -4: "WQ_ERR_UNSUPPORTED", -5: "WQ_ERR_HIP", -6: "WQ_ERR_WORKSPACE", -7: "WQ_ERR_SCRATCH"}
 KERNELS = {"auto": 0, "gemv": 1, "gemm": 2}
 
 # name -> (restype, argtypes) for every symbol declared in include/wq.h
@@ -58,6 +58,8 @@ SIGNATURES = {
     "wq_linear_w4a8_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "wq_linear_w4a8": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _sz,
                                       _vp]),
+    "wq_linear_sparse_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
+                                                _vp, _i32, _vp]),
     "wq_auto_kernel": (ctypes.c_int, [_i64, _i64, _i64]),
     "wq_last_hip_error": (ctypes.c_int, []),
     "wq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -204,6 +206,41 @@ def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, ou
                                      _p(row_ptr), _p(col) if nnz else None, _p(val) if nnz else None, nnz,
                                      _p(out), y_dtype, KERNELS[kernel], _p(workspace), wbytes, _stream(x))
     _check("wq_linear_sparse_kernel", rc)
+    return out
+
+
+def linear_sparse_noalloc(x, packed, scales, zeros, out, row_ptr=None, col=None, val=None, group: int = GROUP):
+    """``linear_sparse`` through ``wq_linear_sparse_noalloc``: no workspace, the
+    library's per-GPU scratch instead; ``out`` (float16 or float32 [M, N]) must be
+    given, so the call allocates nothing."""
+    import torch
+    lib = load()
+    _need(x, torch.float16, "x")
+    _need(packed, torch.int32, "packed")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.float16, "zeros")
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 8 != K or scales.shape != (N, K // group) or zeros.shape != scales.shape:
+        raise ValueError("inconsistent shapes")
+    if out.dtype not in (torch.float16, torch.float32):
+        raise TypeError("out must be float16 or float32")
+    _need(out, out.dtype, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    nnz = 0
+    if row_ptr is not None:
+        _need(row_ptr, torch.int32, "row_ptr")
+        if row_ptr.numel() != N + 1:
+            raise ValueError("row_ptr must have N+1 entries")
+        nnz = int(col.numel()) if col is not None else 0
+        if nnz:
+            _need(col, torch.int32, "col")
+            _need(val, torch.float16, "val")
+    rc = lib.wq_linear_sparse_noalloc(_p(x), M, K, _p(packed), _p(scales), _p(zeros), N, group, _p(row_ptr),
+                                      _p(col) if nnz else None, _p(val) if nnz else None, nnz, _p(out),
+                                      1 if out.dtype == torch.float32 else 0, _stream(x))
+    _check("wq_linear_sparse_noalloc", rc)
     return out
 
 

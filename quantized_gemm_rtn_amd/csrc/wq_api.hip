@@ -8,6 +8,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+// Scratch of wq_linear_sparse_noalloc, in each GPU's memory for the life of the
+// process: the split-K partial sums and the transposed activations of the GEMM.
+// In host code this name only stands in for the symbol: kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[WQ_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int64_t kGroup = 128;
@@ -31,6 +39,29 @@ int hip_status(hipError_t e) {
   if (e == hipSuccess) return WQ_OK;
   last_hip_error = e;
   return WQ_ERR_HIP;
+}
+
+// Device address of `scratch` on each GPU, looked up once per device (with that
+// device current) on its first no-allocation call.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_address[kMaxDevices] = {};
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_address[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_address[dev] = p;
+  }
+  *out = scratch_address[dev];
+  return hipSuccess;
 }
 
 int check_linear_args(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
@@ -94,6 +125,7 @@ const char* wq_status_string(int status) {
     case WQ_ERR_UNSUPPORTED: return "unsupported group size, dtype or kernel choice";
     case WQ_ERR_HIP: return "a HIP kernel launch failed";
     case WQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case WQ_ERR_SCRATCH: return "the product needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -222,6 +254,33 @@ int wq_linear_sparse(const uint16_t* x, int64_t M, int64_t K, const uint32_t* pa
   if (!row_ptr) return WQ_ERR_NULL;
   return wq_linear_sparse_kernel(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
                                  WQ_KERNEL_AUTO, workspace, workspace_bytes, stream);
+}
+
+int wq_linear_sparse_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
+                             const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                             const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz, void* y,
+                             int32_t y_dtype, void* stream) {
+  const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                                   WQ_KERNEL_AUTO);
+  if (rc != WQ_OK) return rc;
+  if (M == 0) return WQ_OK;
+  const int kernel = wq_auto_kernel(M, N, K);
+  const size_t need = kernel == WQ_KERNEL_GEMM ? wq::gemm_workspace_bytes(M, N, K) : 0;
+  if (need > WQ_NOALLOC_SCRATCH_BYTES) return WQ_ERR_SCRATCH;
+  const int y_f32 = y_dtype == WQ_F32;
+  const int32_t* rp = nnz > 0 ? row_ptr : nullptr;
+  hipError_t e;
+  if (kernel == WQ_KERNEL_GEMV) {
+    e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, wq::LowRank{},
+                        as_stream(stream));
+  } else {
+    void* ws = nullptr;
+    e = scratch_of_current_device(&ws);
+    if (e == hipSuccess)
+      e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32, ws, need, wq::LowRank{},
+                          as_stream(stream));
+  }
+  return hip_status(e);
 }
 
 int wq_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         s = lib.wq_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.wq_status_string(-99).decode() == "unknown status"
@@ -286,3 +286,22 @@ def test_no_function_static_state():
             if re.match(r"^\s+static\s+(?!constexpr\b|const\b|_assert|inline\b|hipError_t\b)", line):
                 bad.append(f"{os.path.basename(path)}:{i}: {line.strip()}")
     assert not bad, bad
+
+
+def test_noalloc_validation(lib):
+    """wq_linear_sparse_noalloc checks its arguments like wq_linear_sparse and
+    rejects, before any HIP call, a product whose split GEMM would need more than
+    the scratch it holds per GPU."""
+    f = lib.wq_linear_sparse_noalloc
+    assert f(None, 1, 256, A2, A3, A4, 64, 128, None, None, None, 0, A5, 0, None) == -1
+    assert f(A, 1, 256, A2, A3, A4, 64, 64, None, None, None, 0, A5, 0, None) == -4
+    assert f(A, 1, 100, A2, A3, A4, 64, 128, None, None, None, 0, A5, 0, None) == -2
+    assert f(MIS, 1, 256, A2, A3, A4, 64, 128, None, None, None, 0, A5, 0, None) == -3
+    assert f(None, 0, 256, A2, A3, A4, 64, 128, None, None, None, 0, None, 0, None) == 0   # empty batch
+    # 512 x 16384 x 65536 with a CSR term: the split-K partials plus the transposed
+    # activations exceed WQ_NOALLOC_SCRATCH_BYTES (96 MiB)
+    M, N, K = 512, 16384, 65536
+    assert lib.wq_linear_workspace_bytes(M, N, K) > 96 << 20
+    assert f(A, M, K, A2, A3, A4, N, 128, A, A2, A3, 10, A5, 0, None) == -7
+    # the 70B down-projection at M = 512 with its CSR fits (about 92 MiB)
+    assert lib.wq_linear_workspace_bytes(512, 8192, 28672) <= 96 << 20
