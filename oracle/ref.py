@@ -159,6 +159,63 @@ def unpack(packed: np.ndarray) -> np.ndarray:
     return q.reshape(N, W * 8)
 
 
+# 3-bit packing.  The SqueezeLLM explainer stores models of 3 bits per weight
+# (section 1; the weight-bits option of sections 4.1 and 5.2), and packing is what
+# turns a smaller code into fewer bytes on byte-addressed hardware (AWQ paper,
+# section 1); no page gives a 3-bit layout.  The one used here puts every run of
+# 32 consecutive codes (k = 32u .. 32u + 31) into three words, 96 bits with none
+# wasted.  Within a run, code pair P = 4t + p (t, p = 0..3) is the pair of codes
+# lo = 8t + p and hi = 8t + p + 4.  Pairs 0..14 sit five to a word: pair P in word
+# P // 5, lo at bits [3i, 3i + 3) and hi at bits [16 + 3i, 16 + 3i + 3) with
+# i = P % 5.  Pair 15 (codes 27 and 31) takes the two bits left in each word: bit
+# b of code 27 is bit 15 of word b, bit b of code 31 is bit 31 of word b.
+def _pairs3():
+    """(P, lo offset, hi offset) for the 16 code pairs of a 32-code run."""
+    return [(P, 8 * (P // 4) + P % 4, 8 * (P // 4) + P % 4 + 4) for P in range(16)]
+
+
+def pack3(q: np.ndarray) -> np.ndarray:
+    """Codes of at most 3 bits, uint8 [N, K] (K a multiple of 32), packed to uint32
+    [N, 3K/32] in the layout described above."""
+    q = np.asarray(q, dtype=np.uint8)
+    N, K = q.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    if q.size and q.max() > 7:
+        raise ValueError("3-bit codes must be at most 7")
+    u = q.reshape(N, K // 32, 32).astype(np.uint32)
+    out = np.zeros((N, K // 32, 3), np.uint32)
+    for P, lo, hi in _pairs3():
+        if P < 15:
+            w, i = divmod(P, 5)
+            out[:, :, w] |= (u[:, :, lo] << np.uint32(3 * i)) | (u[:, :, hi] << np.uint32(16 + 3 * i))
+        else:
+            for b in range(3):
+                out[:, :, b] |= (((u[:, :, lo] >> np.uint32(b)) & np.uint32(1)) << np.uint32(15)) | \
+                                (((u[:, :, hi] >> np.uint32(b)) & np.uint32(1)) << np.uint32(31))
+    return out.reshape(N, 3 * K // 32)
+
+
+def unpack3(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack3: uint32 [N, 3K/32] -> uint8 codes [N, K]."""
+    packed = np.asarray(packed, dtype=np.uint32)
+    N, W = packed.shape
+    if W % 3:
+        raise ValueError("a 3-bit row holds a multiple of three words")
+    w = packed.reshape(N, W // 3, 3)
+    q = np.zeros((N, W // 3, 32), np.uint32)
+    for P, lo, hi in _pairs3():
+        if P < 15:
+            j, i = divmod(P, 5)
+            q[:, :, lo] = (w[:, :, j] >> np.uint32(3 * i)) & np.uint32(7)
+            q[:, :, hi] = (w[:, :, j] >> np.uint32(16 + 3 * i)) & np.uint32(7)
+        else:
+            for b in range(3):
+                q[:, :, lo] |= ((w[:, :, b] >> np.uint32(15)) & np.uint32(1)) << np.uint32(b)
+                q[:, :, hi] |= ((w[:, :, b] >> np.uint32(31)) & np.uint32(1)) << np.uint32(b)
+    return q.reshape(N, W // 3 * 32).astype(np.uint8)
+
+
 # --------------------------------------------------------------------------
 # O7-O8: dequantization and the linear layer, float64
 # --------------------------------------------------------------------------
@@ -222,7 +279,7 @@ def linear_ref(x, q, s, z, row_ptr=None, col=None, val=None, group: int = GROUP,
     """y[m, n] = sum_k x[m, k] * w_hat[n, k] + (W_sparse x)[n, m] in float64,
     plus the low-rank branch (x . L1^T . L2^T)[m, n] when the factors are given.
 
-    ``q`` may be the unpacked codes [N, K] (uint8) or the packed words
+    ``q`` may be the unpacked codes [N, K] (uint8) or the 4-bit packed words
     [N, K/8] (uint32)."""
     q = np.asarray(q)
     if q.dtype == np.uint32:

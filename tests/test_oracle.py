@@ -67,13 +67,13 @@ def _on_grid(seed, N, G, group=128):
     return w.reshape(N, G * group), q.reshape(N, G * group).astype(np.uint8), s16, z
 
 
-@pytest.mark.parametrize("seed,N,G", [(0, 3, 1), (1, 8, 4), (2, 5, 7)])
-def test_on_grid_exact_recovery(seed, N, G):
-    w, q, s16, z = _on_grid(seed, N, G)
+@pytest.mark.parametrize("seed,N,G,group", [(0, 3, 1, 128), (1, 8, 4, 128), (2, 5, 7, 128), (3, 6, 8, 64)])
+def test_on_grid_exact_recovery(seed, N, G, group):
+    w, q, s16, z = _on_grid(seed, N, G, group)
     # the construction is exact in float32
-    assert np.array_equal(((q.reshape(N, G, 128) - z[:, :, None]) * s16.astype(np.float64)[:, :, None]).reshape(N, -1),
-                          w.astype(np.float64))
-    q2, s2, z2 = oracle.quantize_rtn(w)
+    assert np.array_equal(((q.reshape(N, G, group) - z[:, :, None]) *
+                           s16.astype(np.float64)[:, :, None]).reshape(N, -1), w.astype(np.float64))
+    q2, s2, z2 = oracle.quantize_rtn(w, group)
     assert np.array_equal(f16_bits(s2), f16_bits(s16))
     assert np.array_equal(z2.astype(np.int64), z)
     assert np.array_equal(q2, q)
@@ -124,7 +124,7 @@ def test_group_minimum_gets_code_zero():
                 assert qg[n, g, amin[n, g]] == 0
 
 
-@pytest.mark.parametrize("group,bits", [(128, 4), (256, 4), (128, 3), (256, 3), (128, 2)])
+@pytest.mark.parametrize("group,bits", [(128, 4), (256, 4), (128, 3), (256, 3), (128, 2), (64, 4), (64, 3)])
 def test_brute_force_exact_rationals(group, bits):
     """Each code is the nearest grid point in exact arithmetic; the scale is the
     fp16 nearest to range/qmax (qmax = 2^bits - 1) and the zero-point the
@@ -548,3 +548,81 @@ def test_fewer_bits_on_grid_weights_come_back(bits):
     q, s, zz = oracle.quantize_rtn(W, 128, bits)
     assert np.array_equal(q, codes.astype(np.uint8)) and np.all(s == np.float16(2.0 ** -6))
     assert np.array_equal(oracle.dequant(q, s, zz), W.astype(np.float64))
+
+
+# ---------------------------------------------------------------- 3-bit packing
+def _pack3_golden():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "pack3_hand_words.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _pack3_golden(), ids=lambda c: c["name"])
+def test_pack3_hand_words(case):
+    """Words derived by hand from the 3-bit layout, for single codes in each kind
+    of slot (a pair's lo and hi half, each word, the split pair 15)."""
+    q = np.zeros((1, 32), np.uint8)
+    if case["codes"] == "all7":
+        q[:] = 7
+    else:
+        for k, v in case["codes"].items():
+            q[0, int(k)] = v
+    words = oracle.pack3(q)
+    assert [int(w) for w in words[0]] == [int(h, 16) for h in case["words"]], case["name"]
+    assert np.array_equal(oracle.unpack3(words), q)
+
+
+def test_pack3_uses_every_bit_once():
+    """Each of the 32 x 3 code bits of a run lands on its own one of the 96 word
+    bits: 0.375 bytes per weight with nothing lost or shared."""
+    seen = set()
+    for k in range(32):
+        for b in range(3):
+            q = np.zeros((1, 32), np.uint8)
+            q[0, k] = 1 << b
+            w = oracle.pack3(q)[0]
+            bits = [(j, i) for j in range(3) for i in range(32) if (int(w[j]) >> i) & 1]
+            assert len(bits) == 1, (k, b, bits)
+            seen.add(bits[0])
+    assert len(seen) == 96
+
+
+def test_pack3_roundtrip_and_size():
+    rng = np.random.default_rng(33)
+    q = rng.integers(0, 8, size=(7, 512)).astype(np.uint8)
+    p = oracle.pack3(q)
+    assert p.shape == (7, 3 * 512 // 32) and p.dtype == np.uint32
+    assert p.nbytes * 8 == q.size * 3
+    assert np.array_equal(oracle.unpack3(p), q)
+    with pytest.raises(ValueError):
+        oracle.pack3(np.full((1, 32), 8, np.uint8))
+
+
+def test_pack3_differs_from_sequential_bits():
+    """The layout is not the plain sequential one (code k at bit 3k of the 96-bit
+    run): a mutant that packed sequentially would still round-trip, so the hand
+    words above are what pin the layout."""
+    q = np.zeros((1, 32), np.uint8)
+    q[0, 1] = 1                                   # sequential: bit 3 of word 0
+    assert int(oracle.pack3(q)[0, 0]) == 1 << 3   # here: pair 1 lo, i = 1 -> bit 3 too
+    q[0, 1], q[0, 5] = 0, 1                       # sequential: bit 15; here: pair 1 hi -> bit 19
+    assert int(oracle.pack3(q)[0, 0]) == 1 << 19
+
+
+def test_group64_is_not_group128():
+    """At 64-channel groups each half of a 128-channel group gets its own range:
+    the metadata has twice the columns, and a group whose halves differ in range
+    gets different scales (a mutant that quantized in 128-channel groups and
+    repeated the metadata would fail this)."""
+    W = workloads.random_weights(64, 2, 256, sigma=0.02)
+    W[0, 0:64] *= 4.0
+    q, s, z = oracle.quantize_rtn(W, 64)
+    assert s.shape == (2, 4)
+    assert float(s[0, 0]) > 2.0 * float(s[0, 1])
+    # each 64-channel half equals the quantizer run on that half alone
+    for g in range(4):
+        qg, sg, zg = oracle.quantize_rtn(W[:, 64 * g:64 * g + 64], 64)
+        assert np.array_equal(q[:, 64 * g:64 * g + 64], qg)
+        assert np.array_equal(f16_bits(s[:, g:g + 1]), f16_bits(sg))
+    # and dequantization at 64 reads the right column
+    w_hat = oracle.dequant(q, s, z, 64)
+    assert np.allclose(w_hat, W, atol=float(s.astype(np.float64).max()) / 2 + 1e-12)
