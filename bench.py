@@ -10,12 +10,14 @@ reported separately under "offline").
 
 Inputs stay resident in HBM: R copies of the layer (packed codes, scales,
 zeros, CSR, x, y) totalling >= 1 GiB are rotated so no launch is served from
-the 256 MB Infinity Cache.  After W warm-up launches, the K timed launches are
-captured in one HIP graph and replayed five times, each between
-synchronizations; HIP events on the launch stream bracket each replay, and the
-median replay gives the figures (p10 and p90 are reported beside them).  The
-default K spans about 20 ms per replay; the other workloads size their replays
-the same way (at least 200 launches and 20 ms, from one timed replay of 20).
+the 256 MB Infinity Cache.  After W warm-up launches, each timed run queues a
+busy-wait kernel and then the K launches; HIP events on the launch stream,
+recorded after the busy-wait and after the last launch, bracket the K launches,
+which the GPU runs back to back (the busy-wait lasts long enough for the host to
+submit them all, and the run checks that it did).  Five runs, between
+synchronizations; the median gives the figures (p10 and p90 beside them).  The
+other workloads size their runs to at least 200 launches and 20 ms, from one
+timed run of 20.
 
 Printed: ONE JSON line with the metric (GB/s, algorithmic bytes), the roofline
 of the dominant kernel, the CPU oracle baseline, and the other workloads
@@ -46,12 +48,14 @@ MFMA_F16_PEAK_TFS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 ROTATE_BYTES = 1 << 30
 
 
-def alg_bytes(M, N, K, nnz, y_bytes=2, rank=0, act_order=False):
-    """Bytes the method must move: packed codes, fp16 scale+zero, CSR, the fp16
-    low-rank factors, the int32 channel permutation of an act-order layer, x, y."""
+def alg_bytes(M, N, K, nnz, y_bytes=2, rank=0, act_order=False, bits=4, group=128):
+    """Bytes the method must move: packed codes (bits / 8 per weight), fp16
+    scale+zero per group, CSR, the fp16 low-rank factors, the int32 channel
+    permutation of an act-order layer, x, y."""
     csr = (6 * nnz + 4 * (N + 1)) if nnz else 0
     perm = 4 * K if act_order else 0
-    return N * K // 2 + N * (K // 128) * 4 + csr + 2 * rank * (K + N) + perm + M * K * 2 + M * N * y_bytes
+    return (N * K * bits // 8 + N * (K // group) * 4 + csr + 2 * rank * (K + N) + perm + M * K * 2 +
+            M * N * y_bytes)
 
 
 def alg_flops(M, N, K, nnz, rank=0):
@@ -61,10 +65,11 @@ def alg_flops(M, N, K, nnz, rank=0):
 class Layer:
     """A quantized layer on the GPU, produced by the library's own quantizer."""
 
-    def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False, w4a8=False):
+    def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False, w4a8=False, bits=4, group=128):
         W, x, cfg = workloads.make(index, M=M, K=K)
         N, K = W.shape
         self.N, self.K, self.M, self.rank, self.act_order, self.w4a8 = N, K, M, rank, act_order, w4a8
+        self.bits, self.group = bits, group
         if w4a8:
             self.outliers = torch.from_numpy(workloads.x_outlier_channels(index, M=M, K=K)).cuda()
             self.ws_bytes = wq.linear_w4a8_workspace_bytes(M, N, K)
@@ -75,8 +80,8 @@ class Layer:
             q = wq.quantize_rtn_act_order(Wd, self.perm, sparse_k=self.sparse_k)
             self.ws_bytes = wq.linear_act_order_workspace_bytes(M, N, K)
         else:
-            q = wq.quantize_rtn(Wd, sparse_k=self.sparse_k)
-        self.packed = wq.pack(q["codes"])
+            q = wq.quantize_rtn(Wd, sparse_k=self.sparse_k, group=group, bits=bits)
+        self.packed = wq.pack(q["codes"], bits=bits)
         self.scales, self.zeros = q["scales"], q["zeros"]
         self.row_ptr, self.col, self.val = q["row_ptr"], q["col"], q["val"]
         del q, Wd
@@ -90,7 +95,8 @@ class Layer:
 
     def sets(self, torch, rotate_bytes):
         """R independent copies of every input/output, R * bytes >= rotate_bytes."""
-        nb = alg_bytes(self.M, self.N, self.K, self.sparse_k, rank=self.rank, act_order=self.act_order)
+        nb = alg_bytes(self.M, self.N, self.K, self.sparse_k, rank=self.rank, act_order=self.act_order,
+                       bits=self.bits, group=self.group)
         R = max(1, min(64, math.ceil(rotate_bytes / nb)))
         out = []
         for r in range(R):
@@ -125,73 +131,78 @@ def launch(wq, s, kernel="auto"):
 
 
 def time_launches(wq, torch, sets, steps, warmup, kernel="auto", repeats=5):
-    """Warm up eagerly, capture `steps` rotating launches in one graph, replay it
-    `repeats` times, each between synchronizations; returns the milliseconds per
-    launch of every replay."""
+    """Warm up, then time `repeats` runs of `steps` launches rotating over the
+    buffer sets; returns the milliseconds per launch of every run."""
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for i in range(warmup):
             launch(wq, sets[i % len(sets)], kernel)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            launch(wq, sets[i % len(sets)], kernel)
-    torch.cuda.synchronize()
-    g.replay()  # untimed replay: first replay uploads the graph
-    torch.cuda.synchronize()
-    per_launch = []
-    for _ in range(repeats):
-        per_launch.append(timed_replay(torch, g, stream) / steps)
-    del g
-    return per_launch
+    return [timed_launches(torch, stream, lambda i: launch(wq, sets[i % len(sets)], kernel), steps) / steps
+            for _ in range(repeats)]
 
 
-# Busy-wait of about 100 us at the engine clock, queued ahead of each timed replay.
-PRIME_CYCLES = 200_000
+# Upper bound of the host's time to submit one launch (measured about 13 us through
+# the binding), used to size the busy-wait that runs ahead of a timed run.
+HOST_US_PER_LAUNCH = 40.0
+ENGINE_GHZ = 2.4  # peak engine clock: the busy-wait lasts at least its cycles / 2.4 GHz
 
 
-def timed_replay(torch, g, stream):
+def timed_launches(torch, stream, fn, steps):
     """Milliseconds between HIP events recorded on `stream` right before and after
-    one replay of graph `g`, between synchronizations. A short busy-wait kernel is
-    queued first, so that the host has submitted the replay before the GPU reaches
-    the start event: the events then bracket the replayed kernels, not the host's
-    graph submission."""
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    `steps` launches fn(0) .. fn(steps - 1), between synchronizations.
+
+    A busy-wait kernel is queued first, long enough for the host to submit all the
+    launches while it runs, so the GPU runs them back to back and the events
+    bracket GPU work only (a graph replay instead adds about 8 us of its own per
+    replay, which a 20-launch run would spread over its launches). The busy-wait
+    itself is timed too: if the host took longer than that to submit, the run
+    raises rather than report host time as GPU time."""
+    prime_us = 200.0 + HOST_US_PER_LAUNCH * steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
-        torch.cuda._sleep(PRIME_CYCLES)
-        start.record(stream)
-        g.replay()
-        end.record(stream)
+        ev[0].record(stream)
+        torch.cuda._sleep(int(prime_us * 1e3 * ENGINE_GHZ))
+        t0 = time.perf_counter()
+        ev[1].record(stream)
+        for i in range(steps):
+            fn(i)
+        ev[2].record(stream)
+        host_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
-    return start.elapsed_time(end)
+    if host_ms > ev[0].elapsed_time(ev[1]):
+        raise RuntimeError(f"host submission ({host_ms:.3f} ms) outlasted the busy-wait "
+                           f"({ev[0].elapsed_time(ev[1]):.3f} ms): the timed run would include host gaps")
+    return ev[1].elapsed_time(ev[2])
 
 
-def replay_length(wq, torch, sets, kernel, min_ms=25.0, min_steps=200, max_steps=20000):
-    """Launches per replay so that one replay spans at least min_steps and about
-    min_ms (25 ms, so that the 20 ms floor holds when the estimate from one timed
-    replay of 20 captured launches runs high)."""
+def run_length(wq, torch, sets, kernel, min_ms=20.0, min_steps=200, max_steps=20000):
+    """Launches per timed run so that one run spans at least min_steps and about
+    min_ms, from one timed run of 20 launches."""
     t = time_launches(wq, torch, sets, 20, 0, kernel, repeats=1)[0]
     return int(min(max_steps, max(min_steps, math.ceil(min_ms / t))))
 
 
 def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5, rank=0, mode=""):
-    """steps = None: enough launches per replay for >= 20 ms (and >= 200 launches);
+    """steps = None: enough launches per run for >= 20 ms (and >= 200 launches);
     rank > 0: with a low-rank branch of that rank; mode "ao": the layer in a
     permuted channel order, x gathered through the permutation; mode "w8": the
     W4A8 product with the configuration's activation outlier channels in fp16
-    (the layer has no CSR then)."""
+    (the layer has no CSR then); mode "b3": 3-bit codes in the 3-bit packing;
+    "g64": one (s, z) per 64 input channels; "b3g64": both."""
     act_order, w4a8 = mode == "ao", mode == "w8"
-    L = Layer(wq, torch, index, M, K, rank, act_order, w4a8)
+    bits = 3 if mode in ("b3", "b3g64") else 4
+    group = 64 if mode in ("g64", "b3g64") else 128
+    L = Layer(wq, torch, index, M, K, rank, act_order, w4a8, bits, group)
     if w4a8:
         L.sparse_k = 0
     sets = L.sets(torch, ROTATE_BYTES)
     if steps is None:
-        steps = replay_length(wq, torch, sets, kernel)
+        steps = run_length(wq, torch, sets, kernel)
     runs = time_launches(wq, torch, sets, steps, warmup, kernel, repeats=replays)
     ms = float(np.median(runs))
-    nb = alg_bytes(M, L.N, L.K, L.sparse_k, rank=rank, act_order=act_order)
+    nb = alg_bytes(M, L.N, L.K, L.sparse_k, rank=rank, act_order=act_order, bits=bits, group=group)
     nf = alg_flops(M, L.N, L.K, L.sparse_k, rank=rank)
     used = kernel if kernel != "auto" else wq.auto_kernel(M, L.N, L.K)
     if w4a8:
@@ -224,14 +235,8 @@ def stream_copy(torch, nbytes, steps=100):
         for i in range(R):
             dst.copy_(bufs[i])
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            dst.copy_(bufs[i % R])
-    g.replay()
-    torch.cuda.synchronize()
-    us = timed_replay(torch, g, stream) / steps * 1e3
-    del g, bufs, dst
+    us = timed_launches(torch, stream, lambda i: dst.copy_(bufs[i % R]), steps) / steps * 1e3
+    del bufs, dst
     torch.cuda.empty_cache()
     return {"bytes_read": n * 4, "bytes_written": n * 4, "us_per_launch": us,
             "GBps_read_plus_write": 2 * n * 4 / (us * 1e-6) / 1e9}
@@ -240,7 +245,7 @@ def stream_copy(torch, nbytes, steps=100):
 def stream_read(torch, nbytes, steps=200):
     """Context for the decode rows: one launch of a plain streaming-read kernel
     (libwq_probe.so) over nbytes, rotating over >= 1 GiB of sources, timed like the
-    layer (graph replays, median of five)."""
+    layer (median of five runs)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "quantized_gemm_rtn_amd", "libwq_probe.so"))
     lib.wq_probe_stream_read.restype = ctypes.c_int
@@ -261,15 +266,9 @@ def stream_read(torch, nbytes, steps=200):
         for i in range(R):
             go(i)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            go(i)
-    g.replay()
-    torch.cuda.synchronize()
-    runs = [timed_replay(torch, g, stream) / steps for _ in range(5)]
+    runs = [timed_launches(torch, stream, go, steps) / steps for _ in range(5)]
     us = float(np.median(runs)) * 1e3
-    del g, bufs
+    del bufs
     torch.cuda.empty_cache()
     return {"bytes_read": nbytes, "us_per_launch": us, "GBps": nbytes / (us * 1e-6) / 1e9,
             "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
@@ -378,10 +377,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3000,
-                    help="launches per timed replay of the headline workload (the default spans about 20 ms)")
+                    help="launches per timed run of the headline workload (the default spans about 20 ms)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--replays", type=int, default=5, help="timed replays per workload (median, p10, p90)")
+    ap.add_argument("--replays", type=int, default=5, help="timed runs per workload (median, p10, p90)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--workloads", default="", help="extra workloads as config:M[:kernel[:K[:rank[:mode]]]],... "
                     "(mode ao: an act-order layer; w8: the W4A8 product) "
@@ -438,12 +437,16 @@ def main():
                      (2, 1, "auto", None, 0, "ao"), (4, 2048, "auto", None, 0, "ao")]
             # the prefill layer as a W4A8 product with its 8 fp16 outlier channels
             plan += [(4, 2048, "auto", None, 0, "w8")]
+            # the decode layers with 3-bit codes and with 64-channel groups
+            plan += [(2, 1, "auto", None, 0, "b3"), (2, 1, "auto", None, 0, "g64"), (2, 1, "auto", None, 0, "b3g64"),
+                     (5, 8, "auto", None, 0, "b3"), (4, 2048, "auto", None, 0, "b3")]
         for index, M, kern, Kov, rank, mode in plan:
             r = measure(wq, torch, index, M, None, args.warmup, kernel=kern, K=Kov, replays=args.replays,
                         rank=rank, mode=mode)
             rows.append(r)
             print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov}{' r=%d' % rank if rank else ''}"
-                  f"{' act-order' if mode == 'ao' else ''}{' w4a8' if mode == 'w8' else ''} "
+                  f"{' act-order' if mode == 'ao' else ''}{' w4a8' if mode == 'w8' else ''}"
+                  f"{' ' + mode if mode in ('b3', 'g64', 'b3g64') else ''} "
                   f"{r['kernel']:4s} "
                   f"{r['us_per_launch']:9.2f} us  "
                   f"{r['GBps']:8.1f} GB/s ({100 * r['hbm_frac']:5.1f}%)  {r['TFLOPs']:7.1f} TF/s "

@@ -20,9 +20,11 @@
  *    overlap.
  *  - State: none between calls, except (a) each GPU's scratch array of
  *    wq_linear_sparse_noalloc and its device address, looked up under a mutex on
- *    the first such call on that GPU, and (b) a per-thread copy of the last HIP
- *    launch error (wq_last_hip_error). Every other entry point is reentrant and
- *    thread-safe.
+ *    the first such call on that GPU, (b) a per-thread copy of the last HIP
+ *    launch error (wq_last_hip_error), and (c) the record, under a mutex, of the
+ *    kernels whose dynamic-LDS limit was already raised on each device (setting
+ *    it costs tens of microseconds per call). Every entry point other than
+ *    wq_linear_sparse_noalloc is reentrant and thread-safe.
  *  - fp16 values travel as uint16_t bit patterns. All arrays are row-major and
  *    contiguous.
  *  - Every argument is validated on the host BEFORE any HIP call; a failed
@@ -75,13 +77,15 @@ size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k);
  * wq_quantize_rtn - offline dense-and-sparse split plus RTN group quantization.
  *
  *  W        [N, K] float32, the weights (output channel n, input channel k).
- *  group    input channels per quantization group: 128, a larger multiple of 128
- *           that divides K, or -1 for one group per row (the default of the
- *           group-size option in the SqueezeLLM explainer, section 5.3);
- *           WQ_ERR_UNSUPPORTED otherwise. The metadata is always written in the
- *           layout the linear entry points read, one (s, z) per 128 channels: a
- *           coarser group's (s, z) is repeated in each of its 128-channel slots,
- *           so the products below take it unchanged (with group = 128).
+ *  group    input channels per quantization group: 64, 128, a larger multiple of
+ *           128 that divides K, or -1 for one group per row (the default of the
+ *           group-size option in the SqueezeLLM explainer, section 5.3, which notes
+ *           that smaller groups cost metadata and may gain accuracy);
+ *           WQ_ERR_UNSUPPORTED otherwise. The metadata is written in the layout the
+ *           linear entry points read: [N, K/64] for group = 64 (products with
+ *           group = 64), else one (s, z) per 128 channels, [N, K/128], a coarser
+ *           group's (s, z) repeated in each of its 128-channel slots (products with
+ *           group = 128).
  *  sparse_k number of entries moved to the sparse fp16 part, 0 <= sparse_k <= N*K.
  *           They are the sparse_k entries of largest |w| (ties: lower flat index
  *           n*K + k first); the SqueezeLLM explainer (section 2.2) keeps such a
@@ -89,9 +93,9 @@ size_t wq_quantize_workspace_bytes(int64_t N, int64_t K, int64_t sparse_k);
  *           a Hessian sensitivity that needs calibration data, here by magnitude.
  *           The dense part is W with those entries set to +0.
  *  codes    [N, K] uint8 out: q = clamp(rint(w / s) + z, 0, 15) for the dense part.
- *  scales   [N, K/128] fp16 out: s = fp16(max(fl32(fl32(max - min) / 15), 2^-14)),
- *           max and min over the group.
- *  zeros    [N, K/128] fp16 out: z = clamp(rint(-min / s), 0, 15), an integer.
+ *  scales   [N, K/128] ([N, K/64] for group = 64) fp16 out:
+ *           s = fp16(max(fl32(fl32(max - min) / 15), 2^-14)), max and min over the group.
+ *  zeros    the same shape, fp16 out: z = clamp(rint(-min / s), 0, 15), an integer.
  *           (All float32 steps are IEEE, correctly rounded, half-to-even.)
  *  row_ptr  [N+1] int32 out, col [sparse_k] int32 out, val [sparse_k] fp16 out:
  *           the sparse part in CSR, rows = output channels, columns ascending.
@@ -125,6 +129,22 @@ int wq_quantize_rtn_bits(const float* W, int64_t N, int64_t K, int32_t group, in
  */
 int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* stream);
 
+/*
+ * wq_pack_bits - wq_pack for bits = 4, or the 3-bit packing for bits = 3 (the
+ * SqueezeLLM explainer's 3-bit models, section 1; packing is what turns a smaller
+ * code into fewer bytes, AWQ paper, section 1; no page gives a 3-bit layout, so
+ * this one is defined here): every run of 32 consecutive codes (k = 32u .. 32u + 31,
+ * K a multiple of 32) takes three words, 3u .. 3u + 2, with no bit unused. Code pair
+ * P = 4t + p (t, p = 0..3) is (lo = code 32u + 8t + p, hi = code 32u + 8t + p + 4);
+ * pairs 0..14 sit in word 3u + P / 5, lo at bits [3i, 3i + 3) and hi at bits
+ * [16 + 3i, 16 + 3i + 3) with i = P % 5; pair 15 puts bit b of code 32u + 27 at
+ * bit 15 and bit b of code 32u + 31 at bit 31 of word 3u + b.
+ *  codes  [N, K] uint8 in (only the low 3 bits of each byte are used for bits = 3).
+ *  packed [N, K/8] (bits = 4) or [N, 3K/32] (bits = 3) uint32 out, 4-byte aligned
+ *         for bits = 3. bits other than 3 or 4: WQ_ERR_UNSUPPORTED.
+ */
+int wq_pack_bits(const uint8_t* codes, int64_t N, int64_t K, int32_t bits, uint32_t* packed, void* stream);
+
 /* Bytes of device workspace with which the linear entry points may split the K
  * dimension of the prefill GEMM across blocks (fp32 partial sums, reduced in a
  * fixed order), for shapes whose output tiles alone cannot fill the GPU, and, for a
@@ -139,7 +159,8 @@ size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * dequantization w_hat[n, k] = (q[n, k] - z[n, k/128]) * s[n, k/128].
  *  x       [M, K] fp16 activations.
  *  packed  [N, K/8] uint32 codes as written by wq_pack.
- *  scales, zeros [N, K/128] fp16 as written by wq_quantize_rtn.
+ *  group   128, or 64 for a layer quantized with 64-channel groups.
+ *  scales, zeros [N, K/group] fp16 as written by wq_quantize_rtn.
  *  y       [M, N] out, fp16 (y_dtype = WQ_F16, one rounding of the fp32
  *          accumulator) or float32 (WQ_F32). Accumulation is fp32.
  *  workspace: device scratch (16-byte aligned) of wq_linear_workspace_bytes(M, N, K)
@@ -166,6 +187,22 @@ int wq_linear_sparse(const uint16_t* x, int64_t M, int64_t K,
                      const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
                      void* y, int32_t y_dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * wq_linear_sparse_bits - wq_linear_sparse_kernel for a layer of 3- or 4-bit codes
+ * (bits), packed by wq_pack_bits with the same bits ([N, 3K/32] words for bits = 3,
+ * the SqueezeLLM explainer's 3-bit models, section 1), with 64- or 128-channel groups
+ * (group, the metadata [N, K/group] of wq_quantize_rtn). A 3-bit layer moves 0.375
+ * bytes of codes per weight instead of 0.5. Every format runs in the decode kernels
+ * (M <= 16) and in the tile GEMM above; only 4-bit codes with 128-channel groups take
+ * the large-M GEMM. row_ptr may be NULL when nnz == 0.
+ *  bits other than 3 or 4, or group other than 64 or 128: WQ_ERR_UNSUPPORTED.
+ */
+int wq_linear_sparse_bits(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, int32_t bits,
+                          const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                          const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
+                          void* y, int32_t y_dtype, int32_t kernel,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * wq_linear_sparse_kernel - wq_linear_sparse with an explicit kernel choice
@@ -254,7 +291,8 @@ size_t wq_quantize_act_order_workspace_bytes(int64_t N, int64_t K, int64_t spars
  * wq_quantize_rtn_act_order - wq_quantize_rtn of W[:, perm] (column i of the copy is
  * column perm[i] of W): the same split, groups, codes, metadata and CSR, all in the
  * permuted channel order (CSR columns are positions in that order; ties of |w| go
- * to the lower flat index in that order).
+ * to the lower flat index in that order). group = 64 is WQ_ERR_UNSUPPORTED here (the
+ * act-order product reads 128-channel metadata).
  *  workspace  required, 256-byte aligned, wq_quantize_act_order_workspace_bytes.
  */
 int wq_quantize_rtn_act_order(const float* W, int64_t N, int64_t K, int32_t group, const int32_t* perm,

@@ -39,10 +39,13 @@ SIGNATURES = {
     "wq_quantize_rtn_bits": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _sz, _vp]),
     "wq_pack": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
+    "wq_pack_bits": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "wq_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "wq_linear": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _sz, _vp]),
     "wq_linear_sparse": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
                                         _vp, _i32, _vp, _sz, _vp]),
+    "wq_linear_sparse_bits": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
+                                             _vp, _i32, _i32, _vp, _sz, _vp]),
     "wq_linear_sparse_kernel": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _i64,
                                                _vp, _i32, _i32, _vp, _sz, _vp]),
     "wq_linear_lowrank_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
@@ -131,7 +134,8 @@ def quantize_rtn(W, sparse_k: int = 0, group: int = GROUP, workspace=None, bits:
     _need(W, torch.float32, "W")
     N, K = W.shape
     dev = W.device
-    G = K // GROUP  # metadata slots per row, whatever the quantization group
+    # metadata slots per row: one per 64 channels for group 64, else one per 128
+    G = K // 64 if group == 64 else K // GROUP
     codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
     scales = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)
     zeros = torch.empty((N, max(G, 1)), dtype=torch.float16, device=dev)
@@ -149,15 +153,38 @@ def quantize_rtn(W, sparse_k: int = 0, group: int = GROUP, workspace=None, bits:
                 col=col[:sparse_k], val=val[:sparse_k])
 
 
-def pack(codes):
-    """Eight INT4 codes per 32-bit word (returned as int32 bit patterns)."""
+def pack(codes, bits: int = 4):
+    """Eight INT4 codes per 32-bit word, or (bits = 3) 32 3-bit codes per three
+    words (returned as int32 bit patterns, [N, K/8] or [N, 3K/32])."""
     import torch
     lib = load()
     _need(codes, torch.uint8, "codes")
     N, K = codes.shape
-    packed = torch.empty((N, K // 8), dtype=torch.int32, device=codes.device)
-    _check("wq_pack", lib.wq_pack(_p(codes), N, K, _p(packed), _stream(codes)))
+    width = K // 8 if bits == 4 else 3 * K // 32
+    packed = torch.empty((N, width), dtype=torch.int32, device=codes.device)
+    _check("wq_pack_bits", lib.wq_pack_bits(_p(codes), N, K, bits, _p(packed), _stream(codes)))
     return packed
+
+
+def _layer_format(packed, scales, K, N):
+    """(bits, group) of a layer from its tensors' shapes: [N, K/8] words are 4-bit
+    codes and [N, 3K/32] 3-bit ones; [N, K/128] metadata is group 128, [N, K/64]
+    group 64."""
+    if packed.shape[0] != N:
+        raise ValueError("inconsistent shapes")
+    if packed.shape[1] * 8 == K:
+        bits = 4
+    elif K % 32 == 0 and packed.shape[1] == 3 * K // 32:
+        bits = 3
+    else:
+        raise ValueError("packed must be [N, K/8] (4-bit) or [N, 3K/32] (3-bit)")
+    if tuple(scales.shape) == (N, K // GROUP):
+        group = GROUP
+    elif tuple(scales.shape) == (N, K // 64):
+        group = 64
+    else:
+        raise ValueError("scales must be [N, K/128] or [N, K/64]")
+    return bits, group
 
 
 def linear_workspace_bytes(M, N, K):
@@ -165,11 +192,13 @@ def linear_workspace_bytes(M, N, K):
 
 
 def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, out_dtype=None,
-                  kernel: str = "auto", out=None, group: int = GROUP, workspace=None):
+                  kernel: str = "auto", out=None, workspace=None):
     """y = x . dequant(packed, scales, zeros)^T (+ W_sparse x when CSR is given).
 
-    ``workspace`` (uint8 device tensor of ``linear_workspace_bytes`` bytes) lets
-    the prefill GEMM split K; when omitted, one is allocated per call."""
+    The layer's format follows from the shapes: 4-bit ([N, K/8] words) or 3-bit
+    ([N, 3K/32]) codes, one (s, z) per 128 ([N, K/128]) or 64 ([N, K/64]) input
+    channels. ``workspace`` (uint8 device tensor of ``linear_workspace_bytes``
+    bytes) lets the GEMM split K; when omitted, one is allocated per call."""
     import torch
     lib = load()
     out_dtype = torch.float16 if out_dtype is None else out_dtype
@@ -179,7 +208,8 @@ def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, ou
     _need(zeros, torch.float16, "zeros")
     M, K = x.shape
     N = packed.shape[0]
-    if packed.shape[1] * 8 != K or scales.shape != (N, K // group) or zeros.shape != scales.shape:
+    bits, group = _layer_format(packed, scales, K, N)
+    if zeros.shape != scales.shape:
         raise ValueError("inconsistent shapes")
     nnz = 0
     if row_ptr is not None:
@@ -202,10 +232,10 @@ def linear_sparse(x, packed, scales, zeros, row_ptr=None, col=None, val=None, ou
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.wq_linear_sparse_kernel(_p(x), M, K, _p(packed), _p(scales), _p(zeros), N, group,
-                                     _p(row_ptr), _p(col) if nnz else None, _p(val) if nnz else None, nnz,
-                                     _p(out), y_dtype, KERNELS[kernel], _p(workspace), wbytes, _stream(x))
-    _check("wq_linear_sparse_kernel", rc)
+    rc = lib.wq_linear_sparse_bits(_p(x), M, K, _p(packed), bits, _p(scales), _p(zeros), N, group,
+                                   _p(row_ptr), _p(col) if nnz else None, _p(val) if nnz else None, nnz,
+                                   _p(out), y_dtype, KERNELS[kernel], _p(workspace), wbytes, _stream(x))
+    _check("wq_linear_sparse_bits", rc)
     return out
 
 
@@ -249,9 +279,8 @@ def last_hip_error() -> int:
     return int(load().wq_last_hip_error())
 
 
-def linear(x, packed, scales, zeros, out_dtype=None, kernel: str = "auto", out=None, group: int = GROUP,
-           workspace=None):
-    return linear_sparse(x, packed, scales, zeros, None, None, None, out_dtype, kernel, out, group, workspace)
+def linear(x, packed, scales, zeros, out_dtype=None, kernel: str = "auto", out=None, workspace=None):
+    return linear_sparse(x, packed, scales, zeros, None, None, None, out_dtype, kernel, out, workspace)
 
 
 def linear_lowrank_workspace_bytes(M, N, K, r):

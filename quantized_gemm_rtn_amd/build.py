@@ -25,7 +25,8 @@ PROBE_LIB = os.path.join(HERE, "libwq_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemm.hip", "lowrank.hip", "actorder.hip", "w4a8.hip"]
+SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemv_fmt.hip", "gemm.hip", "lowrank.hip",
+           "actorder.hip", "w4a8.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -42,7 +43,7 @@ COMMON = [
 PER_FILE = {"quant.hip": ["-ffp-contract=off"], "split.hip": ["-ffp-contract=off"], "w4a8.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # The product kernels must keep everything in registers and LDS: the compiler
 # reports each kernel's per-lane scratch, and any use of it fails the build.
-NO_SCRATCH = {"gemv.hip", "gemm.hip", "lowrank.hip", "w4a8.hip"}
+NO_SCRATCH = {"gemv.hip", "gemv_fmt.hip", "gemm.hip", "lowrank.hip", "w4a8.hip"}
 RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
 
 
@@ -88,7 +89,8 @@ def scratch_users(remarks: str) -> dict:
 
 def _link(objs, lib, verbose):
     tmp = lib + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # no undefined symbols left for the loader to find (a missing object fails here)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

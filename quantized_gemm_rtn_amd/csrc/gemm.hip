@@ -37,6 +37,7 @@
 #include "wq_launch.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace wq {
 
@@ -97,7 +98,10 @@ __device__ __forceinline__ void lowrank_add32(f32x16 (&acc)[MT][NT], const f16* 
 
 // Two waves per SIMD (two blocks per CU): the blocks run out of phase, so one
 // block's waits on memory and barriers are covered by the other's MFMAs.
-template <int BM, int BN, int WGM, int WGN, bool SPARSE>
+// BITS = 3: 3-bit codes, 32 per three words (a lane reads one 12-byte run per K
+// step instead of four words); G64: one (s, z) per 64 input channels, which is one
+// per K step.
+template <int BM, int BN, int WGM, int WGN, bool SPARSE, int BITS = 4, bool G64 = false>
 __global__ void __launch_bounds__(64 * WGM * WGN, 2)
 gemm_kernel(GemmArgs a) {
   constexpr int T = 64 * WGM * WGN;
@@ -112,8 +116,9 @@ gemm_kernel(GemmArgs a) {
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int M = a.M, N = a.N, K = a.K;
-  const int G = K >> 7;
-  const int KW8 = K >> 3;
+  const int Gs = G64 ? K >> 6 : K >> 7;     // (s, z) per row
+  const int RW = BITS == 4 ? K >> 3 : 3 * (K >> 5);  // words per row
+  typedef typename std::conditional<BITS == 4, uint4, uint3>::type WT;
 
   // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous
   // range of logical tiles, M fastest, so tiles that share weight columns meet in
@@ -142,19 +147,20 @@ gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int n = min(n0 + wn * WTN + j * 32 + (lane & 31), N - 1);
-    woff[j] = n * (int)KW8 + 4 * h;
-    soff[j] = n * G;
+    woff[j] = n * RW + (BITS == 4 ? 4 : 3) * h;
+    soff[j] = n * Gs;
   }
 
-  uint4 xr[XV], wr[NT];
+  uint4 xr[XV];
+  WT wr[NT];
   f16 sr[NT], zr[NT];
   auto load_step = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < XV; ++i) xr[i] = *reinterpret_cast<const uint4*>(a.x + xoff[i] + k0);
-    const int g = k0 >> 7;
+    const int g = G64 ? k0 >> 6 : k0 >> 7;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      wr[j] = *reinterpret_cast<const uint4*>(a.packed + woff[j] + (k0 >> 3));
+      wr[j] = *reinterpret_cast<const WT*>(a.packed + woff[j] + (BITS == 4 ? k0 >> 3 : 3 * (k0 >> 5)));
       sr[j] = a.scales[soff[j] + g];
       zr[j] = a.zeros[soff[j] + g];
     }
@@ -236,7 +242,7 @@ gemm_kernel(GemmArgs a) {
     store_x(smem);
   }
   __syncthreads();
-  uint4 wc[NT];
+  WT wc[NT];
   f16 sc[NT], zc[NT];
   for (int s = 0; s < nk; ++s) {
     const int k0 = kb + s * kBK;
@@ -261,8 +267,13 @@ gemm_kernel(GemmArgs a) {
         const f16 zb = (f16)1024.0f + zc[j], zn = -((f16)64.0f + zc[j]);
         const f16x2 bias = {zb, zb}, nbias16 = {zn, zn};
         const f16x2 s2 = {sc[j], sc[j]};
-        const uint32_t w = ks == 0 ? wc[j].x : ks == 1 ? wc[j].y : ks == 2 ? wc[j].z : wc[j].w;
-        uint4 d = dequant_word_x16(w, magic, bias, nbias16, s2);
+        uint4 d;
+        if constexpr (BITS == 4) {
+          const uint32_t w = ks == 0 ? wc[j].x : ks == 1 ? wc[j].y : ks == 2 ? wc[j].z : wc[j].w;
+          d = dequant_word_x16(w, magic, bias, nbias16, s2);
+        } else {
+          d = dequant3(wc[j], ks, magic, bias, s2);
+        }
         // sparse entries of this column inside this lane's eight input channels
         // [kc, kc + 8) are added to the dequantized weight (entries below kc belong
         // to the other half-wave's channels and are skipped)
@@ -828,21 +839,21 @@ static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
   return plan_gemm_kind(M, N, K, sparse);
 }
 
-// enough for the dense and the sparse plan of the shape
+// enough for the dense and the sparse plan of the shape, and for the tile kernel's
+// plan (the one the other weight formats take)
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const size_t a = plan_workspace(plan_gemm(M, N, K, false), M, N, K);
   const size_t b = plan_workspace(plan_gemm(M, N, K, true), M, N, K);
-  return a > b ? a : b;
+  const size_t c = plan_workspace(plan_gemm_kind(M, N, K, true), M, N, K);
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
 template <int BM, int BN, int WGM, int WGN, int MINB, int WS>
 static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
   constexpr size_t lds = 2 * (size_t)BM * kBigSS * sizeof(f16) + kBigSzBytes;
   auto kern = gemm_big_kernel<BM, BN, WGM, WGN, MINB, WS>;
-  // set on every launch (per device, cheap; no state kept between calls)
   {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
   }
   a.tiles_m = (a.M + BM - 1) / BM;
@@ -852,13 +863,12 @@ static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, bool SPARSE>
+template <int BM, int BN, int WGM, int WGN, bool SPARSE, int BITS = 4, bool G64 = false>
 static hipError_t launch_tile(GemmArgs a, hipStream_t stream) {
   constexpr size_t lds = 2 * (size_t)BM * kLdsStride * sizeof(f16);
-  auto kern = gemm_kernel<BM, BN, WGM, WGN, SPARSE>;
+  auto kern = gemm_kernel<BM, BN, WGM, WGN, SPARSE, BITS, G64>;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
   }
   a.tiles_m = (a.M + BM - 1) / BM;
@@ -866,17 +876,30 @@ static hipError_t launch_tile(GemmArgs a, hipStream_t stream) {
   const int64_t nblk = (int64_t)a.tiles_m * a.tiles_n * a.ksplit;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * WGM * WGN), lds, stream, a);
   return hipGetLastError();
+}
+
+// tile kernel for a weight format other than 4-bit codes with 128-channel groups
+static hipError_t launch_tile_fmt(const GemmArgs& a, int bm, bool sp, WFormat f, hipStream_t stream) {
+#define WQ_TF(BM, SP, B, G6) \
+  if (bm == BM && sp == SP && f.bits == B && f.g64 == G6) return launch_tile<BM, 256, 1, 4, SP, B, G6>(a, stream);
+#define WQ_TF_F(BM, SP) WQ_TF(BM, SP, 4, true) WQ_TF(BM, SP, 3, false) WQ_TF(BM, SP, 3, true)
+  WQ_TF_F(64, true) WQ_TF_F(64, false) WQ_TF_F(128, true) WQ_TF_F(128, false)
+#undef WQ_TF_F
+#undef WQ_TF
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,
-                       size_t workspace_bytes, const LowRank& lr, hipStream_t stream) {
+                       size_t workspace_bytes, const LowRank& lr, hipStream_t stream, WFormat f) {
   constexpr int64_t kRowsPerLaunch = (int64_t)1 << 20;  // keeps the block count within int range
   for (int64_t m = 0; m < M; m += kRowsPerLaunch) {
     const int64_t mc = M - m < kRowsPerLaunch ? M - m : kRowsPerLaunch;
     const bool sp = row_ptr != nullptr;
-    GemmPlan p = plan_gemm(mc, N, K, sp);
+    // the other weight formats run in the tile kernel (its K step of 64 channels is
+    // one 64-channel group, or two 3-bit runs per lane pair), the CSR term inside it
+    GemmPlan p = f.plain() ? plan_gemm(mc, N, K, sp) : plan_gemm_kind(mc, N, K, true);
     if (p.sparse_in_reduce && (workspace == nullptr || workspace_bytes < plan_workspace(p, mc, N, K)))
       p = plan_gemm_kind(mc, N, K, true);  // too small a workspace: the sparse term inside gemm_kernel
     const size_t need = plan_workspace(p, mc, N, K);
@@ -928,6 +951,8 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
       e = launch_big<64, 256, 1, 4, 2, 4>(a, stream);
     else if (p.kind == 2)
       e = launch_big<64, 256, 1, 4, 2, 2>(a, stream);
+    else if (!f.plain())
+      e = launch_tile_fmt(a, p.bm, sp_kernel, f, stream);
     else if (p.bm == 64)
       e = sp_kernel ? launch_tile<64, 256, 1, 4, true>(a, stream) : launch_tile<64, 256, 1, 4, false>(a, stream);
     else

@@ -31,12 +31,18 @@
 
 namespace wq {
 
-// COARSE = false: groups of 128 (gc == 1 at compile time)
-template <bool COARSE>
+// Groups of 64 channels (a smaller group, which the same section of the SqueezeLLM
+// explainer says trades metadata for accuracy) are quantized two per wave: lanes
+// 0..31 hold one group and lanes 32..63 the next, the min/max butterfly stays
+// within each half, and the metadata is [N, K/64].
+//
+// MODE 0: groups of 128 (gc == 1 at compile time); 1: coarser groups; 2: groups of 64
+template <int MODE>
 __global__ void __launch_bounds__(256)
 rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ mask, int64_t N, int64_t K,
                     int64_t gc_arg, float qmax, uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                     uint16_t* __restrict__ zeros) {
+  constexpr bool COARSE = MODE == 1;
   const int lane = threadIdx.x & 63;
   const int64_t gc = COARSE ? gc_arg : 1;
   const int64_t G = K / kGroup;  // 128-channel metadata slots per row
@@ -68,7 +74,7 @@ rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ ma
       mx = fmaxf(mx, fmaxf(v.x, v.y));
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
+    for (int o = MODE == 2 ? 16 : 32; o >= 1; o >>= 1) {
       mn = fminf(mn, __shfl_xor(mn, o));
       mx = fmaxf(mx, __shfl_xor(mx, o));
     }
@@ -88,9 +94,11 @@ rtn_quantize_kernel(const float* __restrict__ W, const uint32_t* __restrict__ ma
       t1 = fminf(fmaxf(t1, 0.0f), qmax);
       const uint32_t q0 = (uint32_t)t0, q1 = (uint32_t)t1;
       *reinterpret_cast<uint16_t*>(codes + off) = (uint16_t)(q0 | (q1 << 8));
-      if (lane == 0) {
-        scales[n * G + g0 + c] = __builtin_bit_cast(uint16_t, s16);
-        zeros[n * G + g0 + c] = __builtin_bit_cast(uint16_t, (f16)(float)zi);
+      if (MODE == 2 ? (lane & 31) == 0 : lane == 0) {
+        // with groups of 64, slot 2 (g0 + c) + (lane >> 5) of a [N, K/64] row
+        const int64_t slot = MODE == 2 ? n * 2 * G + 2 * (g0 + c) + (lane >> 5) : n * G + g0 + c;
+        scales[slot] = __builtin_bit_cast(uint16_t, s16);
+        zeros[slot] = __builtin_bit_cast(uint16_t, (f16)(float)zi);
       }
     }
   }
@@ -109,6 +117,32 @@ pack_kernel(const uint8_t* __restrict__ codes, int64_t nwords, uint32_t* __restr
   }
 }
 
+// 32 codes (one per byte, low three bits used) -> three words, in the layout of
+// wq_pack_bits: pair P = 4t + p = (code 8t + p, code 8t + p + 4); pairs 0..14 five to a
+// word at bits 3i and 16 + 3i (i = P % 5), pair 15's bits in bit 15 (code 27) and
+// bit 31 (code 31) of each word.
+__global__ void __launch_bounds__(256)
+pack3_kernel(const uint8_t* __restrict__ codes, int64_t nruns, uint32_t* __restrict__ packed) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nruns; i += stride) {
+    const uint4 c0 = *reinterpret_cast<const uint4*>(codes + 32 * i);
+    const uint4 c1 = *reinterpret_cast<const uint4*>(codes + 32 * i + 16);
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const auto code = [&](int k) { return (cw[k >> 2] >> (8 * (k & 3))) & 7u; };
+    uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int P = 0; P < 15; ++P) {
+      const int lo = 8 * (P >> 2) + (P & 3);
+      w[P / 5] |= (code(lo) << (3 * (P % 5))) | (code(lo + 4) << (16 + 3 * (P % 5)));
+    }
+#pragma unroll
+    for (int b = 0; b < 3; ++b) w[b] |= (((code(27) >> b) & 1u) << 15) | (((code(31) >> b) & 1u) << 31);
+    packed[3 * i] = w[0];
+    packed[3 * i + 1] = w[1];
+    packed[3 * i + 2] = w[2];
+  }
+}
+
 static int64_t clamp_blocks(int64_t want) { return want < 1 ? 1 : (want > 65536 ? 65536 : want); }
 
 hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int64_t K, int64_t group, int bits,
@@ -117,11 +151,21 @@ hipError_t launch_quantize(const float* W, const uint32_t* mask, int64_t N, int6
   const int64_t groups = N * (K / group);
   const int64_t blocks = clamp_blocks((groups + 3) / 4);
   if (group == kGroup)
-    hipLaunchKernelGGL(rtn_quantize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
+    hipLaunchKernelGGL(rtn_quantize_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
                        (int64_t)1, qmax, codes, scales, zeros);
+  else if (group == 64)  // one wave per pair of groups
+    hipLaunchKernelGGL(rtn_quantize_kernel<2>, dim3((unsigned)clamp_blocks((groups / 2 + 3) / 4)), dim3(256), 0,
+                       stream, W, mask, N, K, (int64_t)1, qmax, codes, scales, zeros);
   else
-    hipLaunchKernelGGL(rtn_quantize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
+    hipLaunchKernelGGL(rtn_quantize_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, W, mask, N, K,
                        group / kGroup, qmax, codes, scales, zeros);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack3(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream) {
+  const int64_t nruns = N * (K / 32);
+  const int64_t blocks = clamp_blocks((nruns + 255) / 256);
+  hipLaunchKernelGGL(pack3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, nruns, packed);
   return hipGetLastError();
 }
 

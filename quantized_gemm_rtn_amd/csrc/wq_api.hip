@@ -8,7 +8,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <map>
 #include <mutex>
+#include <utility>
 
 // Scratch of wq_linear_sparse_noalloc, in each GPU's memory for the life of the
 // process: the split-K partial sums and the transposed activations of the GEMM.
@@ -64,16 +66,18 @@ hipError_t scratch_of_current_device(void** out) {
   return hipSuccess;
 }
 
+// group: the (s, z) slot width the products read, 128 (every product) or 64 (the
+// entry points that take 64-channel groups pass allow_g64)
 int check_linear_args(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, const uint16_t* scales,
                       const uint16_t* zeros, int64_t N, int32_t group, const int32_t* row_ptr,
                       const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int32_t y_dtype,
-                      int32_t kernel) {
+                      int32_t kernel, bool allow_g64 = false) {
   // M = 0 (an empty batch) is valid and computes nothing; x and y may then be NULL
   if (!packed || !scales || !zeros) return WQ_ERR_NULL;
   if (M != 0 && (!x || !y)) return WQ_ERR_NULL;
   if (row_ptr == nullptr && nnz != 0) return WQ_ERR_NULL;
   if (nnz > 0 && (!col || !val)) return WQ_ERR_NULL;
-  if (group != kGroup) return WQ_ERR_UNSUPPORTED;
+  if (group != kGroup && !(allow_g64 && group == 64)) return WQ_ERR_UNSUPPORTED;
   if (y_dtype != WQ_F16 && y_dtype != WQ_F32) return WQ_ERR_UNSUPPORTED;
   if (kernel != WQ_KERNEL_AUTO && kernel != WQ_KERNEL_GEMV && kernel != WQ_KERNEL_GEMM) return WQ_ERR_UNSUPPORTED;
   if (M < 0 || N < 1 || K < kGroup || K % kGroup != 0) return WQ_ERR_SHAPE;
@@ -92,9 +96,9 @@ int check_quantize_args(const float* W, int64_t N, int64_t K, int32_t group, int
   if (!W || !codes || !scales || !zeros) return WQ_ERR_NULL;
   if (sparse_k > 0 && (!row_ptr || !col || !val)) return WQ_ERR_NULL;
   if (N < 1 || K < kGroup || K % kGroup != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
-  // quantization group: a multiple of 128 that divides K, or -1 for one group per row
+  // quantization group: 64, a multiple of 128 that divides K, or -1 for one group per row
   const int64_t g = group == -1 ? K : group;
-  if (g < kGroup || g % kGroup != 0 || K % g != 0) return WQ_ERR_UNSUPPORTED;
+  if (g != 64 && (g < kGroup || g % kGroup != 0 || K % g != 0)) return WQ_ERR_UNSUPPORTED;
   if (sparse_k < 0 || sparse_k > N * K) return WQ_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 2)) return WQ_ERR_ALIGN;
   if ((row_ptr && !aligned(row_ptr, 4)) || (col && !aligned(col, 4)) || (val && !aligned(val, 2)))
@@ -110,7 +114,24 @@ int check_quantize_args(const float* W, int64_t N, int64_t K, int32_t group, int
 // the permuted copy of W or x at the start of an act-order workspace
 size_t act_order_copy_bytes(int64_t rows, int64_t K, size_t elem) { return ((size_t)rows * K * elem + 255) / 256 * 256; }
 
+// (kernel, device) -> the dynamic-LDS limit already set there
+std::mutex lds_mutex;
+std::map<std::pair<const void*, int>, size_t> lds_limit;
+
 }  // namespace
+
+hipError_t wq::set_dynamic_lds(const void* kern, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(lds_mutex);
+  const auto key = std::make_pair(kern, dev);
+  const auto it = lds_limit.find(key);
+  if (it != lds_limit.end() && it->second >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) lds_limit[key] = bytes;
+  return e;
+}
 
 extern "C" {
 
@@ -165,10 +186,17 @@ int wq_quantize_rtn(const float* W, int64_t N, int64_t K, int32_t group, int64_t
 }
 
 int wq_pack(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, void* stream) {
+  return wq_pack_bits(codes, N, K, 4, packed, stream);
+}
+
+int wq_pack_bits(const uint8_t* codes, int64_t N, int64_t K, int32_t bits, uint32_t* packed, void* stream) {
   if (!codes || !packed) return WQ_ERR_NULL;
-  if (N < 1 || K < 8 || K % 8 != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
-  if (!aligned(codes, 16) || !aligned(packed, 16)) return WQ_ERR_ALIGN;
-  return hip_status(wq::launch_pack(codes, N, K, packed, as_stream(stream)));
+  if (bits != 3 && bits != 4) return WQ_ERR_UNSUPPORTED;
+  const int64_t unit = bits == 4 ? 8 : 32;
+  if (N < 1 || K < unit || K % unit != 0 || N >= kMax32 / K) return WQ_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(packed, bits == 4 ? 16 : 4)) return WQ_ERR_ALIGN;
+  const hipStream_t s = as_stream(stream);
+  return hip_status(bits == 4 ? wq::launch_pack(codes, N, K, packed, s) : wq::launch_pack3(codes, N, K, packed, s));
 }
 
 size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -183,27 +211,40 @@ int wq_auto_kernel(int64_t M, int64_t N, int64_t K) {
   return M <= 16 ? WQ_KERNEL_GEMV : WQ_KERNEL_GEMM;
 }
 
+int wq_linear_sparse_bits(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, int32_t bits,
+                          const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
+                          const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz, void* y,
+                          int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                                   kernel, true);
+  if (rc != WQ_OK) return rc;
+  if (bits != 3 && bits != 4) return WQ_ERR_UNSUPPORTED;
+  if (bits == 3 && !aligned(packed, 4)) return WQ_ERR_ALIGN;
+  if (M == 0) return WQ_OK;
+  if (kernel == WQ_KERNEL_AUTO) kernel = wq_auto_kernel(M, N, K);
+  const int y_f32 = y_dtype == WQ_F32;
+  const int32_t* rp = nnz > 0 ? row_ptr : nullptr;  // nnz == 0: the dense product
+  wq::WFormat f;
+  f.bits = bits;
+  f.g64 = group == 64;
+  hipError_t e;
+  if (kernel == WQ_KERNEL_GEMV)
+    e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, wq::LowRank{},
+                        as_stream(stream), f);
+  else
+    e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32,
+                        workspace != nullptr && aligned(workspace, 16) ? workspace : nullptr, workspace_bytes,
+                        wq::LowRank{}, as_stream(stream), f);
+  return hip_status(e);
+}
+
 int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                             const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
                             const int32_t* row_ptr, const int32_t* col, const uint16_t* val, int64_t nnz,
                             void* y, int32_t y_dtype, int32_t kernel, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  const int rc = check_linear_args(x, M, K, packed, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
-                                   kernel);
-  if (rc != WQ_OK) return rc;
-  if (M == 0) return WQ_OK;
-  if (kernel == WQ_KERNEL_AUTO) kernel = wq_auto_kernel(M, N, K);
-  const int y_f32 = y_dtype == WQ_F32;
-  const int32_t* rp = nnz > 0 ? row_ptr : nullptr;  // nnz == 0: the dense product
-  hipError_t e;
-  if (kernel == WQ_KERNEL_GEMV)
-    e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, wq::LowRank{},
-                        as_stream(stream));
-  else
-    e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32,
-                        workspace != nullptr && aligned(workspace, 16) ? workspace : nullptr, workspace_bytes,
-                        wq::LowRank{}, as_stream(stream));
-  return hip_status(e);
+  return wq_linear_sparse_bits(x, M, K, packed, 4, scales, zeros, N, group, row_ptr, col, val, nnz, y, y_dtype,
+                               kernel, workspace, workspace_bytes, stream);
 }
 
 size_t wq_linear_lowrank_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -300,6 +341,7 @@ int wq_quantize_rtn_act_order(const float* W, int64_t N, int64_t K, int32_t grou
                               int32_t* row_ptr, int32_t* col, uint16_t* val, void* workspace,
                               size_t workspace_bytes, void* stream) {
   if (!perm) return WQ_ERR_NULL;
+  if (group == 64) return WQ_ERR_UNSUPPORTED;  // the act-order product reads 128-channel metadata
   // W's own checks stand in for those of the permuted copy, which lives in the workspace
   const size_t copy = act_order_copy_bytes(N, K, 4);
   char* ws = static_cast<char*>(workspace);

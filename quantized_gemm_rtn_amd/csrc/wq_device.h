@@ -127,6 +127,46 @@ __device__ __forceinline__ uint4 dequant_word_nat(uint32_t w, uint32_t magic, f1
   return uint4{r[0], r[1], r[2], r[3]};
 }
 
+// ---------------------------------------------------------------------------
+// 3-bit codes. A run of 32 consecutive codes is packed into three words (the
+// layout of wq_pack_bits): code pair P = 4t + p (t, p = 0..3) is (8t + p, 8t + p + 4),
+// the pair that register p of MFMA step t holds in the perm_x8 order above; pairs
+// 0..14 sit five to a word (pair P in word P / 5 at bits 3i and 16 + 3i, i = P % 5),
+// pair 15 in the top bit of each half-word (bit b of code 27 at bit 15 of word b,
+// of code 31 at bit 31). So a lane that loads one run (12 bytes) holds the B
+// operands of four MFMA steps, like the four words of a 4-bit run, and each pair
+// comes out as (1024 + q_lo, 1024 + q_hi) in two instructions (six for pair 15).
+__device__ __forceinline__ uint32_t pair3_biased(const uint3& w, int P, uint32_t magic) {
+  if (P < 15) {
+    const uint32_t x = P < 5 ? w.x : (P < 10 ? w.y : w.z);
+    const int i = P % 5;
+    return and_or(i ? x >> (3 * i) : x, 0x00070007u, magic);
+  }
+  uint32_t v = and_or(w.x >> 15, 0x00010001u, magic);
+  v = and_or(w.y >> 14, 0x00020002u, v);
+  return and_or(w.z >> 13, 0x00040004u, v);
+}
+
+// The four fp16 pairs (1024 + q) of MFMA step t (codes 8t .. 8t + 7 in perm_x8 order).
+__device__ __forceinline__ uint4 codes3_biased(const uint3& w, int t, uint32_t magic) {
+  return uint4{pair3_biased(w, 4 * t, magic), pair3_biased(w, 4 * t + 1, magic), pair3_biased(w, 4 * t + 2, magic),
+               pair3_biased(w, 4 * t + 3, magic)};
+}
+
+// Exact fp16 q - z of MFMA step t (bias = 1024 + z in both halves).
+__device__ __forceinline__ uint4 codes3_minus_zero(const uint3& w, int t, uint32_t magic, f16x2 bias) {
+  const uint4 b = codes3_biased(w, t, magic);
+  return uint4{as_u32(as_f16x2(b.x) - bias), as_u32(as_f16x2(b.y) - bias), as_u32(as_f16x2(b.z) - bias),
+               as_u32(as_f16x2(b.w) - bias)};
+}
+
+// fp16 (q - z) * s of MFMA step t: the subtraction is exact, the multiply rounds once.
+__device__ __forceinline__ uint4 dequant3(const uint3& w, int t, uint32_t magic, f16x2 bias, f16x2 s) {
+  const uint4 b = codes3_biased(w, t, magic);
+  return uint4{as_u32((as_f16x2(b.x) - bias) * s), as_u32((as_f16x2(b.y) - bias) * s),
+               as_u32((as_f16x2(b.z) - bias) * s), as_u32((as_f16x2(b.w) - bias) * s)};
+}
+
 // Slot of element j (0..7) of a chunk of eight after perm_x8.
 __device__ __forceinline__ int perm_slot(int j) { return ((j & 3) << 1) | (j >> 2); }
 

@@ -8,6 +8,11 @@
 
 namespace wq {
 
+// Raises kernel `kern`'s dynamic-LDS limit to `bytes` on the current device, once:
+// hipFuncSetAttribute costs tens of microseconds of host time per call, so the
+// (kernel, device) pairs already raised are remembered (under a mutex).
+hipError_t set_dynamic_lds(const void* kern, size_t bytes);
+
 // Workspace carved up by the outlier split.
 struct SplitWorkspace {
   uint32_t* hist;     // [2048] radix histogram
@@ -55,10 +60,26 @@ size_t lowrank_partial_bytes(int64_t M, int64_t K, int64_t r);
 hipError_t launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* L1, int64_t r,
                                float* part, uint16_t* t, hipStream_t stream);
 
+// Weight format of a product: 4-bit codes (eight per word) or 3-bit codes (32 per
+// three words, the layout of wq_pack_bits), with one (s, z) per 128 or per 64 input
+// channels ([N, K/128] or [N, K/64] metadata).
+struct WFormat {
+  int bits = 4;
+  bool g64 = false;
+  bool plain() const { return bits == 4 && !g64; }
+};
+
 hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
-                       hipStream_t stream);
+                       hipStream_t stream, WFormat f = WFormat{});
+// the same for the formats other than 4-bit with 128-channel groups (no low-rank branch)
+hipError_t launch_gemv_fmt(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
+                           const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
+                           const int32_t* col, const uint16_t* val, void* y, int y_f32, WFormat f,
+                           hipStream_t stream);
+// packing of 3-bit codes: [N, K] bytes -> [N, 3K/32] words (K a multiple of 32)
+hipError_t launch_pack3(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream);
 // The GEMM splits K through `workspace` (fp32 partials) when its tile grid alone
 // cannot fill the GPU and the workspace holds gemm_workspace_bytes(M, N, K);
 // otherwise it runs unsplit.
@@ -66,6 +87,6 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,
-                       size_t workspace_bytes, const LowRank& lr, hipStream_t stream);
+                       size_t workspace_bytes, const LowRank& lr, hipStream_t stream, WFormat f = WFormat{});
 
 }  // namespace wq
