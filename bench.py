@@ -10,14 +10,15 @@ reported separately under "offline").
 
 Inputs stay resident in HBM: R copies of the layer (packed codes, scales,
 zeros, CSR, x, y) totalling >= 1 GiB are rotated so no launch is served from
-the 256 MB Infinity Cache.  After W warm-up launches, each timed run queues a
-busy-wait kernel and then the K launches; HIP events on the launch stream,
-recorded after the busy-wait and after the last launch, bracket the K launches,
-which the GPU runs back to back (the busy-wait lasts long enough for the host to
-submit them all, and the run checks that it did).  Five runs, between
-synchronizations; the median gives the figures (p10 and p90 beside them).  The
-other workloads size their runs to at least 200 launches and 20 ms, from one
-timed run of 20.
+the 256 MB Infinity Cache.  After W warm-up launches, the K timed launches go
+in chunks of at most 256, each queued behind a busy-wait kernel; HIP events on
+the launch stream, recorded after the busy-wait and after the chunk's last
+launch, bracket the chunk, which the GPU runs back to back (the busy-wait lasts
+long enough for the host to submit the chunk, and the run checks that it did).
+The value is the sum over the chunks: the GPU time of exactly K launches.  Five
+runs, between synchronizations; the median gives the figures (p10 and p90
+beside them).  The other workloads size their runs to at least 200 launches and
+20 ms, from one timed run of 20.
 
 Printed: ONE JSON line with the metric (GB/s, algorithmic bytes), the roofline
 of the dominant kernel, the CPU oracle baseline, and the other workloads
@@ -134,53 +135,73 @@ def time_launches(wq, torch, sets, steps, warmup, kernel="auto", repeats=5):
     """Warm up, then time `repeats` runs of `steps` launches rotating over the
     buffer sets; returns the milliseconds per launch of every run."""
     stream = torch.cuda.Stream()
+    host_us = 0.0
     with torch.cuda.stream(stream):
         for i in range(warmup):
+            t0 = time.perf_counter()
             launch(wq, sets[i % len(sets)], kernel)
+            if i > 0:  # the first launch of a kernel also loads it
+                host_us = max(host_us, (time.perf_counter() - t0) * 1e6)
     torch.cuda.synchronize()
-    return [timed_launches(torch, stream, lambda i: launch(wq, sets[i % len(sets)], kernel), steps) / steps
+    return [timed_launches(torch, stream, lambda i: launch(wq, sets[i % len(sets)], kernel), steps,
+                           host_us or HOST_US_PER_LAUNCH) / steps
             for _ in range(repeats)]
 
 
-# Upper bound of the host's time to submit one launch (measured about 13 us through
-# the binding), used to size the busy-wait that runs ahead of a timed run.
+# Host time to submit one launch when none was measured (about 13 us through the
+# binding for one kernel), used to size the busy-wait that runs ahead of a timed run.
 HOST_US_PER_LAUNCH = 40.0
 ENGINE_GHZ = 2.4  # peak engine clock: the busy-wait lasts at least its cycles / 2.4 GHz
+CHUNK = 256       # launches per busy-wait (at most three kernels each: well inside the queue)
 
 
-def timed_launches(torch, stream, fn, steps):
-    """Milliseconds between HIP events recorded on `stream` right before and after
-    `steps` launches fn(0) .. fn(steps - 1), between synchronizations.
+def timed_launches(torch, stream, fn, steps, host_us=HOST_US_PER_LAUNCH):
+    """Milliseconds of GPU time of `steps` launches fn(0) .. fn(steps - 1) on
+    `stream`, between synchronizations.
 
-    A busy-wait kernel is queued first, long enough for the host to submit all the
-    launches while it runs, so the GPU runs them back to back and the events
-    bracket GPU work only (a graph replay instead adds about 8 us of its own per
-    replay, which a 20-launch run would spread over its launches). The busy-wait
-    itself is timed too: if the host took longer than that to submit, the run
-    raises rather than report host time as GPU time."""
-    prime_us = 200.0 + HOST_US_PER_LAUNCH * steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        torch.cuda._sleep(int(prime_us * 1e3 * ENGINE_GHZ))
-        t0 = time.perf_counter()
-        ev[1].record(stream)
-        for i in range(steps):
-            fn(i)
-        ev[2].record(stream)
-        host_ms = (time.perf_counter() - t0) * 1e3
-    torch.cuda.synchronize()
-    if host_ms > ev[0].elapsed_time(ev[1]):
-        raise RuntimeError(f"host submission ({host_ms:.3f} ms) outlasted the busy-wait "
-                           f"({ev[0].elapsed_time(ev[1]):.3f} ms): the timed run would include host gaps")
-    return ev[1].elapsed_time(ev[2])
+    The launches go in chunks of at most CHUNK. Each chunk is queued behind a
+    busy-wait kernel long enough for the host to submit the whole chunk while it
+    runs, and HIP events recorded after the busy-wait and after the chunk's last
+    launch bracket it, so the GPU runs the chunk back to back and the events see
+    GPU work only (a graph replay instead adds about 8 us of its own per replay,
+    which a 20-launch run would spread over its launches). Chunks keep the queue
+    from filling up, which would stall the host until the busy-wait ends. The
+    busy-wait is timed too: if the host took longer than that to submit a chunk,
+    the run raises rather than report host time as GPU time. Returns the sum over
+    the chunks."""
+    total = 0.0
+    for c0 in range(0, steps, CHUNK):
+        n = min(CHUNK, steps - c0)
+        prime_us = 500.0 + 3.0 * max(host_us, 10.0) * n
+        for attempt in range(4):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            with torch.cuda.stream(stream):
+                torch.cuda.synchronize()
+                ev[0].record(stream)
+                torch.cuda._sleep(int(prime_us * 1e3 * ENGINE_GHZ))
+                t0 = time.perf_counter()
+                ev[1].record(stream)
+                for i in range(c0, c0 + n):
+                    fn(i)
+                ev[2].record(stream)
+                host_ms = (time.perf_counter() - t0) * 1e3
+            torch.cuda.synchronize()
+            if host_ms <= ev[0].elapsed_time(ev[1]):
+                break
+            # the host fell behind (a slow host, or a tracer): the chunk is discarded
+            # and run again behind a busy-wait twice as long
+            prime_us *= 2
+        else:
+            raise RuntimeError(f"host submission ({host_ms:.3f} ms) outlasted the busy-wait "
+                               f"({ev[0].elapsed_time(ev[1]):.3f} ms): the timed run would include host gaps")
+        total += ev[1].elapsed_time(ev[2])
+    return total
 
 
 def run_length(wq, torch, sets, kernel, min_ms=20.0, min_steps=200, max_steps=20000):
     """Launches per timed run so that one run spans at least min_steps and about
     min_ms, from one timed run of 20 launches."""
-    t = time_launches(wq, torch, sets, 20, 0, kernel, repeats=1)[0]
+    t = time_launches(wq, torch, sets, 20, 3, kernel, repeats=1)[0]  # warm: a kernel's first launch loads it
     return int(min(max_steps, max(min_steps, math.ceil(min_ms / t))))
 
 
@@ -386,6 +407,9 @@ def main():
                     "(mode ao: an act-order layer; w8: the W4A8 product) "
                     "(default: the batched-decode, prefill and 70B-sweep set)")
     ap.add_argument("--no-offline", action="store_true", help="skip timing the offline quantizer")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="time only the --workloads rows, each for --steps launches per run, and print them as one "
+                         "JSON line (for per-row kernel traces and counters)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one device-to-device copy of BYTES first (reference for counter runs)")
     args = ap.parse_args()
@@ -407,6 +431,20 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.rows_only:
+        out = []
+        for item in args.workloads.split(","):
+            f = item.split(":")
+            mode = f[5] if len(f) > 5 else ""
+            r = measure(wq, torch, int(f[0]), int(f[1]), args.steps, args.warmup,
+                        kernel=f[2] if len(f) > 2 and f[2] else "auto", K=int(f[3]) if len(f) > 3 and f[3] else None,
+                        replays=args.replays, rank=int(f[4]) if len(f) > 4 and f[4] else 0, mode=mode)
+            print(f"# {item} {r['kernel']} {r['us_per_launch']:.2f} us {r['GBps']:.1f} GB/s "
+                  f"{r['TFLOPs']:.1f} TF/s", file=sys.stderr, flush=True)
+            out.append(r)
+        print(json.dumps({"rows": out}), flush=True)
+        return
 
     head = measure(wq, torch, 2, 1, args.steps, args.warmup, replays=args.replays)
     print(f"# headline 2:1 {head['kernel']} {head['us_per_launch']:.2f} us  {head['GBps']:.1f} GB/s "

@@ -66,7 +66,9 @@ typedef enum {
 typedef enum { WQ_F16 = 0, WQ_F32 = 1 } wq_dtype;
 
 /* Kernel choice for the linear entry points. AUTO uses the decode GEMV for
- * M <= 16 and the MFMA GEMM above; the others force one kernel at any M. */
+ * M <= 16, and up to M = 64 also when the GEMM's launch for the shape would have
+ * fewer than 128 blocks (a small layer, whose GEMM cannot fill the GPU), the MFMA
+ * GEMM otherwise; the others force one kernel at any M. */
 typedef enum { WQ_KERNEL_AUTO = 0, WQ_KERNEL_GEMV = 1, WQ_KERNEL_GEMM = 2 } wq_kernel;
 
 /* Bytes of device workspace wq_quantize_rtn needs (0 when sparse_k == 0).
@@ -358,7 +360,8 @@ int wq_linear_w4a8(const uint16_t* x, int64_t M, int64_t K, const int32_t* outli
                    const uint32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N, int32_t group,
                    void* y, int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The kernel WQ_KERNEL_AUTO picks for M rows (WQ_KERNEL_GEMV or WQ_KERNEL_GEMM). */
+/* The kernel WQ_KERNEL_AUTO picks for an M x N x K product (WQ_KERNEL_GEMV or
+ * WQ_KERNEL_GEMM; see wq_kernel). */
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K);
 
 /* A static, NUL-terminated description of a wq_status value. */

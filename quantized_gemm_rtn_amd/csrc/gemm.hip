@@ -839,6 +839,13 @@ static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
   return plan_gemm_kind(M, N, K, sparse);
 }
 
+// blocks of the dense product's GEMM launch for this shape (given a full workspace)
+int64_t gemm_grid_blocks(int64_t M, int64_t N, int64_t K) {
+  const GemmPlan p = plan_gemm(M, N, K, false);
+  const int64_t bm = p.kind == 1 ? 128 : p.bm;
+  return ((M + bm - 1) / bm) * ((N + p.bn - 1) / p.bn) * p.ksplit;
+}
+
 // enough for the dense and the sparse plan of the shape, and for the tile kernel's
 // plan (the one the other weight formats take)
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {

@@ -205,10 +205,16 @@ size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return wq::gemm_workspace_bytes(M, N, K);
 }
 
+// The decode kernels re-read the weights once per 16 rows, the GEMM reads them once
+// but needs a grid that fills the GPU. Measured on the 4096 x 4096 layer with its
+// CSR (the GEMM splits K at most twice there: 32 blocks), the decode kernel stays
+// faster up to M = 64 (25.8 against 35.1 us); on the 8192 x 28672 layer (256
+// blocks) the GEMM takes over from M = 20 (67.5 against 76.6 us).
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K) {
-  (void)N;
-  (void)K;
-  return M <= 16 ? WQ_KERNEL_GEMV : WQ_KERNEL_GEMM;
+  if (M <= 16) return WQ_KERNEL_GEMV;
+  if (M <= 64 && N >= 1 && K >= kGroup && K % kGroup == 0 && wq::gemm_grid_blocks(M, N, K) < 128)
+    return WQ_KERNEL_GEMV;
+  return WQ_KERNEL_GEMM;
 }
 
 int wq_linear_sparse_bits(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed, int32_t bits,

@@ -84,6 +84,8 @@ hipError_t launch_pack3(const uint8_t* codes, int64_t N, int64_t K, uint32_t* pa
 // cannot fill the GPU and the workspace holds gemm_workspace_bytes(M, N, K);
 // otherwise it runs unsplit.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// blocks of the dense GEMM's launch for M x N x K (split K included)
+int64_t gemm_grid_blocks(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,

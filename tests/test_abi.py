@@ -57,7 +57,13 @@ def test_status_strings(lib):
 def test_auto_kernel(lib):
     assert lib.wq_auto_kernel(1, 11008, 4096) == 1
     assert lib.wq_auto_kernel(16, 4096, 4096) == 1
-    assert lib.wq_auto_kernel(17, 4096, 4096) == 2
+    # measured crossover: the 4096 x 4096 layer keeps the decode kernel up to M = 64
+    # (its GEMM grid is 32 blocks), the 70B down-projection switches at M = 17
+    assert lib.wq_auto_kernel(17, 4096, 4096) == 1
+    assert lib.wq_auto_kernel(64, 4096, 4096) == 1
+    assert lib.wq_auto_kernel(65, 4096, 4096) == 2
+    assert lib.wq_auto_kernel(17, 8192, 28672) == 2
+    assert lib.wq_auto_kernel(64, 8192, 28672) == 2
     assert lib.wq_auto_kernel(2048, 14336, 4096) == 2
 
 
