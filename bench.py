@@ -463,10 +463,12 @@ def main():
             plan = [(3, 16, "auto", None, 0, ""), (4, 2048, "auto", None, 0, ""),
                     (5, 1, "auto", None, 0, ""), (5, 8, "auto", None, 0, ""),
                     (5, 64, "auto", None, 0, ""), (5, 512, "auto", None, 0, "")]
-            # the other kernel on either side of the crossover
+            # the other kernel on either side of the crossover, and the MFMA decode
+            # kernel where a single row takes the single-row kernel
             for M in (8, 64):
                 other = "gemm" if wq.auto_kernel(M, 8192, 28672) == "gemv" else "gemv"
                 plan.append((5, M, other, None, 0, ""))
+            plan.append((5, 1, "gemv_mfma", None, 0, ""))
             # one GPU's shard of the 70B down-projection split over 8 GPUs along K
             # (K / 8 = 3584 input channels, 28 groups)
             plan += [(5, 1, "auto", 3584, 0, ""), (5, 512, "auto", 3584, 0, "")]

@@ -69,7 +69,12 @@ typedef enum { WQ_F16 = 0, WQ_F32 = 1 } wq_dtype;
  * M <= 16, and up to M = 64 also when the GEMM's launch for the shape would have
  * fewer than 128 blocks (a small layer, whose GEMM cannot fill the GPU), the MFMA
  * GEMM otherwise; the others force one kernel at any M. */
-typedef enum { WQ_KERNEL_AUTO = 0, WQ_KERNEL_GEMV = 1, WQ_KERNEL_GEMM = 2 } wq_kernel;
+typedef enum { WQ_KERNEL_AUTO = 0, WQ_KERNEL_GEMV = 1, WQ_KERNEL_GEMM = 2, WQ_KERNEL_GEMV_MFMA = 3 } wq_kernel;
+/* WQ_KERNEL_GEMV picks among the decode kernels by shape: for a single row of a long
+ * layer (M = 1, K a multiple of 2048 from 12288 to 32768, 4-bit codes, 128-channel
+ * groups, no low-rank branch) the single-row kernel, whole rows per wave on the
+ * vector units; else the MFMA decode kernels. WQ_KERNEL_GEMV_MFMA forces the MFMA decode kernels (for
+ * measuring one against the other). */
 
 /* Bytes of device workspace wq_quantize_rtn needs (0 when sparse_k == 0).
  * Returns 0 for invalid sizes as well; wq_quantize_rtn reports those. */

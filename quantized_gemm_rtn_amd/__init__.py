@@ -29,7 +29,7 @@ GROUP = 128
 WQ_OK = 0
 STATUS = {0: "WQ_OK", -1: "WQ_ERR_NULL", -2: "WQ_ERR_SHAPE", -3: "WQ_ERR_ALIGN",
           -4: "WQ_ERR_UNSUPPORTED", -5: "WQ_ERR_HIP", -6: "WQ_ERR_WORKSPACE", -7: "WQ_ERR_SCRATCH"}
-KERNELS = {"auto": 0, "gemv": 1, "gemm": 2}
+KERNELS = {"auto": 0, "gemv": 1, "gemm": 2, "gemv_mfma": 3}
 
 # name -> (restype, argtypes) for every symbol declared in include/wq.h
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t

@@ -25,8 +25,8 @@ PROBE_LIB = os.path.join(HERE, "libwq_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemv_fmt.hip", "gemm.hip", "lowrank.hip",
-           "actorder.hip", "w4a8.hip"]
+SOURCES = ["wq_api.hip", "split.hip", "quant.hip", "gemv.hip", "gemv_fmt.hip", "gemv_dot.hip", "gemm.hip",
+           "lowrank.hip", "actorder.hip", "w4a8.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -43,7 +43,7 @@ COMMON = [
 PER_FILE = {"quant.hip": ["-ffp-contract=off"], "split.hip": ["-ffp-contract=off"], "w4a8.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # The product kernels must keep everything in registers and LDS: the compiler
 # reports each kernel's per-lane scratch, and any use of it fails the build.
-NO_SCRATCH = {"gemv.hip", "gemv_fmt.hip", "gemm.hip", "lowrank.hip", "w4a8.hip"}
+NO_SCRATCH = {"gemv.hip", "gemv_fmt.hip", "gemv_dot.hip", "gemm.hip", "lowrank.hip", "w4a8.hip"}
 RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
 
 

@@ -4,6 +4,8 @@
 
 namespace wq {
 
+constexpr int64_t kDotMinK = 12288;  // the single-row kernel from this K on (see launch_gemv)
+
 template <int XC, int SZV, int MR, bool SP>
 static hipError_t launch_lds(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                              const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
@@ -29,8 +31,13 @@ static hipError_t launch_ring(const uint16_t* x, int64_t M, int64_t K, const uin
 hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
-                       hipStream_t stream, WFormat f) {
+                       hipStream_t stream, WFormat f, bool mfma_only) {
   if (!f.plain()) return launch_gemv_fmt(x, M, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, f, stream);
+  // one activation row of a long layer: whole rows per wave and VALU dot products
+  // (gemv_dot.hip). Measured at M = 1 (single-row against MFMA kernel, us): K = 4096
+  // 7.0 / 6.7, 8192 11.1 / 9.8, 14336 14.7 / 15.3, 28672 26.6 / 30.0.
+  if (!mfma_only && lr.r == 0 && K >= kDotMinK && gemv_dot_supported(M, K, scales, zeros))
+    return launch_gemv_dot(x, K, packed, scales, zeros, N, row_ptr, col, val, y, y_f32, stream);
   const int64_t G = K / kGroup;
   // a CSR is passed only with nnz >= 1: its kernels may read entry 0 of an empty row
   const bool sp = row_ptr != nullptr;

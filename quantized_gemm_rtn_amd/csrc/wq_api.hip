@@ -79,7 +79,9 @@ int check_linear_args(const uint16_t* x, int64_t M, int64_t K, const uint32_t* p
   if (nnz > 0 && (!col || !val)) return WQ_ERR_NULL;
   if (group != kGroup && !(allow_g64 && group == 64)) return WQ_ERR_UNSUPPORTED;
   if (y_dtype != WQ_F16 && y_dtype != WQ_F32) return WQ_ERR_UNSUPPORTED;
-  if (kernel != WQ_KERNEL_AUTO && kernel != WQ_KERNEL_GEMV && kernel != WQ_KERNEL_GEMM) return WQ_ERR_UNSUPPORTED;
+  if (kernel != WQ_KERNEL_AUTO && kernel != WQ_KERNEL_GEMV && kernel != WQ_KERNEL_GEMM &&
+      kernel != WQ_KERNEL_GEMV_MFMA)
+    return WQ_ERR_UNSUPPORTED;
   if (M < 0 || N < 1 || K < kGroup || K % kGroup != 0) return WQ_ERR_SHAPE;
   if (nnz < 0 || nnz >= kMax32) return WQ_ERR_SHAPE;
   if (N >= kMax32 / K || M >= kMax32 / K || M >= kMax32 / N) return WQ_ERR_SHAPE;
@@ -234,9 +236,9 @@ int wq_linear_sparse_bits(const uint16_t* x, int64_t M, int64_t K, const uint32_
   f.bits = bits;
   f.g64 = group == 64;
   hipError_t e;
-  if (kernel == WQ_KERNEL_GEMV)
+  if (kernel == WQ_KERNEL_GEMV || kernel == WQ_KERNEL_GEMV_MFMA)
     e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, wq::LowRank{},
-                        as_stream(stream), f);
+                        as_stream(stream), f, kernel == WQ_KERNEL_GEMV_MFMA);
   else
     e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32,
                         workspace != nullptr && aligned(workspace, 16) ? workspace : nullptr, workspace_bytes,
@@ -286,7 +288,7 @@ int wq_linear_lowrank(const uint16_t* x, int64_t M, int64_t K, const uint32_t* p
   const wq::LowRank lr{t, L2, r};
   hipError_t e = wq::launch_lowrank_down(x, M, K, L1, r, part, t, as_stream(stream));
   if (e != hipSuccess) return hip_status(e);
-  if (kernel == WQ_KERNEL_GEMV)
+  if (kernel == WQ_KERNEL_GEMV || kernel == WQ_KERNEL_GEMV_MFMA)
     e = wq::launch_gemv(x, M, K, packed, scales, zeros, N, rp, col, val, y, y_f32, lr, as_stream(stream));
   else
     e = wq::launch_gemm(x, M, K, packed, scales, zeros, N, rp, col, val, nnz, y, y_f32, gws, gws_bytes, lr,

@@ -69,15 +69,23 @@ struct WFormat {
   bool plain() const { return bits == 4 && !g64; }
 };
 
+// mfma_only: never the single-row kernel (the MFMA decode kernels at every M)
 hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
-                       hipStream_t stream, WFormat f = WFormat{});
+                       hipStream_t stream, WFormat f = WFormat{}, bool mfma_only = false);
 // the same for the formats other than 4-bit with 128-channel groups (no low-rank branch)
 hipError_t launch_gemv_fmt(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                            const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                            const int32_t* col, const uint16_t* val, void* y, int y_f32, WFormat f,
                            hipStream_t stream);
+// the single-row decode kernel (whole rows per wave, VALU dot products): for M = 1,
+// K a multiple of 2048 up to 32768, 4-bit codes with 128-channel groups, 16-byte
+// aligned scales and zeros
+bool gemv_dot_supported(int64_t M, int64_t K, const uint16_t* scales, const uint16_t* zeros);
+hipError_t launch_gemv_dot(const uint16_t* x, int64_t K, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* zeros, int64_t N, const int32_t* row_ptr, const int32_t* col,
+                           const uint16_t* val, void* y, int y_f32, hipStream_t stream);
 // packing of 3-bit codes: [N, K] bytes -> [N, 3K/32] words (K a multiple of 32)
 hipError_t launch_pack3(const uint8_t* codes, int64_t N, int64_t K, uint32_t* packed, hipStream_t stream);
 // The GEMM splits K through `workspace` (fp32 partials) when its tile grid alone

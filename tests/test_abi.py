@@ -90,7 +90,7 @@ def linear(lib, x=A, M=1, K=256, packed=A2, scales=A3, zeros=A4, N=64, group=128
     (dict(x=None), -1), (dict(packed=None), -1), (dict(scales=None), -1), (dict(zeros=None), -1),
     (dict(y=None), -1), (dict(nnz=5, row_ptr=None), -1), (dict(row_ptr=A, nnz=3, col=None, val=A2), -1),
     (dict(row_ptr=A, nnz=3, col=A2, val=None), -1),
-    (dict(group=32), -4), (dict(group=256), -4), (dict(y_dtype=2), -4), (dict(kernel=3), -4),
+    (dict(group=32), -4), (dict(group=256), -4), (dict(y_dtype=2), -4), (dict(kernel=4), -4),
     (dict(M=-1), -2), (dict(N=0), -2), (dict(K=0), -2), (dict(K=100), -2), (dict(K=64), -2),
     (dict(nnz=-1, row_ptr=A), -2), (dict(M=1 << 20, K=4096), -2), (dict(N=1 << 20, K=4096), -2),
     (dict(x=MIS), -3), (dict(packed=MIS), -3), (dict(scales=ctypes.c_void_p(0x7F0000000001)), -3),

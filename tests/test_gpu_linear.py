@@ -285,3 +285,29 @@ def test_sparse_split_under_graph_capture(gpu_lib):
         again = call()
         torch.cuda.synchronize()
         assert torch.equal(again, eager), i
+
+
+@pytest.mark.parametrize("N,K", [(300, 12288), (17, 14336), (1000, 16384), (40, 28672), (1, 12288)])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_single_row_kernel(gpu_lib, N, K, sparse):
+    """M = 1 with K a multiple of 2048 from 12288 on runs the single-row kernel
+    (whole rows per wave, even and odd chunk counts, ragged N, a CSR term)."""
+    import torch
+    W = workloads.random_weights(N + K, N, K)
+    L = oracle.quantize_layer(W, N * K // 250 if sparse else 0)
+    x = workloads.random_x(N + 3 * K, 1, K)
+    _full_check(gpu_lib, torch, L, x, "auto", sparse=sparse, label="single row")
+
+
+@pytest.mark.parametrize("K", [12288, 14336, 28672])
+def test_single_row_kernel_integer_exact(gpu_lib, K):
+    """The integer-exact case through the single-row kernel: bit-identical fp32."""
+    import torch
+    N = 70
+    x, q, s, z, rp, col, val = workloads.integer_case(K + 9, 1, N, K, nnz_per_row=7)
+    L = dict(q=q, s=s, z=z, packed=oracle.pack(q), row_ptr=rp, col=col, val=val)
+    D = layer_to_dev(L, torch)
+    say(f"[exact single row] K={K}")
+    y = run_linear(gpu_lib, to_dev(x, torch), D, kernel="gemv", out_dtype=torch.float32)
+    ref = oracle.linear_ref(x, q, s, z, rp, col, val)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
