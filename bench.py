@@ -316,13 +316,18 @@ def measure_offline(wq, torch, index):
     return dict(config=index, N=N, K=K, sparse_k=sk, ms=ms, weights_per_s=N * K / (ms * 1e-3))
 
 
+DECODE_SOURCES = ("gemv_kernels.h", "gemv.hip", "wq_device.h")
+
+
 def kernel_source_hash():
-    """Short hash of the decode kernel source: a recorded traffic figure only
-    describes the kernel it was measured on."""
+    """Short hash of the sources of the headline's decode kernel: a recorded traffic
+    figure only describes the kernel it was measured on."""
     import hashlib
-    path = os.path.join(ROOT, "quantized_gemm_rtn_amd", "csrc", "gemv.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "quantized_gemm_rtn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic():
