@@ -69,6 +69,7 @@ class Layer:
     def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False, w4a8=False, bits=4, group=128):
         W, x, cfg = workloads.make(index, M=M, K=K)
         N, K = W.shape
+        self.wq = wq
         self.N, self.K, self.M, self.rank, self.act_order, self.w4a8 = N, K, M, rank, act_order, w4a8
         self.bits, self.group = bits, group
         if w4a8:
@@ -113,6 +114,10 @@ class Layer:
             if self.w4a8:
                 s.update(outliers=self.outliers.clone(),
                          ws=torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda"))
+            if not (self.rank or self.act_order or self.w4a8):
+                # the plain product's split-K partials, allocated once per set (not per launch)
+                nws = self.wq.linear_workspace_bytes(self.M, self.N, self.K)
+                s["ws"] = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
             out.append(s)
         return out
 
@@ -128,7 +133,7 @@ def launch(wq, s, kernel="auto"):
                           s["val"], out=s["y"], kernel=kernel, workspace=s["ws"])
     else:
         wq.linear_sparse(s["x"], s["packed"], s["scales"], s["zeros"], s["row_ptr"], s["col"], s["val"],
-                         out=s["y"], kernel=kernel)
+                         out=s["y"], kernel=kernel, workspace=s["ws"])
 
 
 def time_launches(wq, torch, sets, steps, warmup, kernel="auto", repeats=5):

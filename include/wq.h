@@ -37,7 +37,8 @@
  *  - Integer sizes: 1 <= N, 0 <= M, K a positive multiple of 128, N*K < 2^31.
  *    M = 0 (an empty batch) returns WQ_OK without launching anything; x and y
  *    may then be NULL.
- *  - Alignment: W, x, codes and packed must be 16-byte aligned (WQ_ERR_ALIGN).
+ *  - Alignment: W, x, codes and packed must be 16-byte aligned, the output y of a
+ *    linear product 4-byte aligned (WQ_ERR_ALIGN).
  */
 #ifndef WQ_H
 #define WQ_H

@@ -311,3 +311,30 @@ def test_single_row_kernel_integer_exact(gpu_lib, K):
     y = run_linear(gpu_lib, to_dev(x, torch), D, kernel="gemv", out_dtype=torch.float32)
     ref = oracle.linear_ref(x, q, s, z, rp, col, val)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [(1, 101, 4096, "gemv"), (7, 101, 4096, "gemv"), (1, 70, 12288, "gemv"),
+                                          (64, 301, 4096, "gemm"), (200, 301, 1024, "gemm")])
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+def test_output_at_4_byte_offset(gpu_lib, M, N, K, kernel, out_dtype):
+    """y 4 bytes past a 16-byte boundary (the least alignment the entry points
+    accept) with M * N not a multiple of 4, through the block-staged, per-wave
+    staging and single-row decode kernels and the split and large-M GEMMs (with a
+    CSR term): right values, and nothing written outside y."""
+    import torch
+    dt = torch.float16 if out_dtype == "f16" else torch.float32
+    off = 4 // dt.itemsize
+    W = workloads.random_weights(N + K + M, N, K)
+    L = oracle.quantize_layer(W, N * K // 200)
+    x = workloads.random_x(M + 2 * N, M, K)
+    D = layer_to_dev(L, torch)
+    buf = torch.full((M * N + off + 3,), 7.0, dtype=dt, device="cuda")
+    y = buf[off:off + M * N].view(M, N)
+    say(f"[offset output] M={M} N={N} K={K} kernel={kernel} {out_dtype}")
+    gpu_lib.linear_sparse(to_dev(x, torch), D["packed"], D["scales"], D["zeros"], D["row_ptr"], D["col"], D["val"],
+                          out_dtype=dt, kernel=kernel, out=y)
+    torch.cuda.synchronize()
+    assert (buf[:off] == 7.0).all() and (buf[off + M * N:] == 7.0).all()
+    ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], L["row_ptr"], L["col"], L["val"])
+    err = oracle.rel_err_inf(y.float().cpu().numpy(), ref)
+    assert err <= TOL, err
