@@ -21,7 +21,8 @@
 //        sum (q - z) x s = s (P - (1024 + z) S_even - (64 + z) S_odd),
 //    with S_even, S_odd the lane's sums of its even and odd activations.
 //  - Sparse term: the lanes of a wave split each of its rows' CSR entries (entry
-//    e0 + l + 64 u for lane l) and add val * x into the same per-row accumulators.
+//    e0 + l + 64 u for lane l) and add val * x into the same per-row accumulators;
+//    each lane's first entry of each row is loaded in the prologue.
 //  - Each row's 64 lane sums are reduced in a fixed order (xor butterfly); no atomics.
 #include "gemv_kernels.h"
 
@@ -42,10 +43,10 @@ gemv_dot_kernel(const f16* __restrict__ x, int K, const uint32_t* __restrict__ p
   constexpr int R = kDotRows, D = kDotDepth, T = 64 * kDotWaves;
   extern __shared__ __align__(16) char smem[];
   const int G = K >> 7;
-  // LDS: (s, 1024 + z) of the block's 16 rows, sz[16][G + 1] | x [K], permuted per 8,
+  // LDS: (s, 1024 + z) of the block's rows, sz[rows][G + 1] | x [K], permuted per 8,
   // odd channels / 16
   f16x2* sz = reinterpret_cast<f16x2*>(smem);
-  f16* xs = reinterpret_cast<f16*>(smem + (size_t)16 * (G + 1) * 4);
+  f16* xs = reinterpret_cast<f16*>(smem + (size_t)kDotWaves * R * (G + 1) * 4);
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int nb = blockIdx.x * kDotWaves * R;  // first row of the block
@@ -76,9 +77,12 @@ gemv_dot_kernel(const f16* __restrict__ x, int K, const uint32_t* __restrict__ p
     const size_t ro = (size_t)(min(n0 + r, N - 1) - min(n0, N - 1)) * rstride;
     wbuf[slot] = *reinterpret_cast<const uint4*>(wrow + ro + (size_t)i * (kDotChunk / 8));
   };
-  // the block's (s, z), staged like the MFMA decode kernels (16 rows from nb)
-  SzStage<8, T> szs;
-  szs.load(scales, zeros, min(nb, N - 1), N, G, t);
+  // the block's (s, z), staged like the MFMA decode kernels, 16 rows at a time
+  constexpr int SZB = kDotWaves * R / 16;
+  static_assert(SZB * 16 == kDotWaves * R, "the block's rows are whole sets of 16");
+  SzStage<8, T> szs[SZB];
+#pragma unroll
+  for (int b = 0; b < SZB; ++b) szs[b].load(scales, zeros, min(nb + 16 * b, N - 1), N, G, t);
   // x staging loads, then the first D steps of weights, then the staging stores (the
   // staging indices are clamped, not tested: a clamped thread rewrites the last vector)
   const int xvecs = K >> 3;
@@ -97,7 +101,24 @@ gemv_dot_kernel(const f16* __restrict__ x, int K, const uint32_t* __restrict__ p
     p.w = as_u32(as_f16x2(p.w) * sixteenth);
     *reinterpret_cast<uint4*>(xs + 8 * min(t + u * T, xvecs - 1)) = p;
   }
-  szs.store(sz, scales, zeros, min(nb, N - 1), N, G, t);
+#pragma unroll
+  for (int b = 0; b < SZB; ++b)
+    szs[b].store(sz + (size_t)16 * b * (G + 1), scales, zeros, min(nb + 16 * b, N - 1), N, G, t);
+  // the lane's first CSR entry of each row (entry e0 + lane), behind the weights: the
+  // rows' bounds have arrived with the staged activations, and the sum after the main
+  // loop then waits for no global load (the 70B down-projection has 14 entries per
+  // row, so one per lane covers nearly every row). Indices are clamped into the row,
+  // or to entry 0 for an empty row (the kernel takes a CSR only with nnz >= 1).
+  int hc[R];
+  f16 hv[R];
+  if constexpr (SP) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = max(min(e0[r] + lane, e1[r] - 1), 0);
+      hc[r] = col[e];
+      hv[r] = val[e];
+    }
+  }
   __syncthreads();
   const f16x2* szw = sz + (size_t)(wave * R) * (G + 1) + (lane >> 2);  // this lane's group column
 
@@ -158,16 +179,19 @@ gemv_dot_kernel(const f16* __restrict__ x, int K, const uint32_t* __restrict__ p
   for (int d = 0; d < D; ++d)
     if (j + d < J) step(j + d, d);
 
-  // sparse term: lane l takes entries e0 + l, e0 + l + 64, ... of each row
+  // sparse term: lane l takes entries e0 + l, e0 + l + 64, ... of each row (the
+  // first from the registers loaded in the prologue)
   if constexpr (SP) {
+    const auto add = [&](int r, int c, float v) {
+      const f16 xc = xs[(c & ~7) | perm_slot(c & 7)];
+      acc[r] += ((c & 1) ? 16.0f * v : v) * (float)xc;  // odd channels were stored / 16
+    };
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      for (int e = e0[r] + lane; e < e1[r]; e += 64) {
-        const int c = col[e];
-        const float v = (float)val[e];
-        const f16 xc = xs[(c & ~7) | perm_slot(c & 7)];
-        acc[r] += ((c & 1) ? 16.0f * v : v) * (float)xc;  // odd channels were stored / 16
-      }
+      if (e0[r] + lane < e1[r]) add(r, hc[r], (float)hv[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      for (int e = e0[r] + lane + 64; e < e1[r]; e += 64) add(r, col[e], (float)val[e]);
   }
   // fixed-order sum over the 64 lanes: DPP scans inside each 16-lane row (totals in
   // lanes 15, 31, 47, 63), then the four row totals in order; lane r stores row n0 + r
@@ -201,7 +225,7 @@ bool gemv_dot_supported(int64_t M, int64_t K, const uint16_t* scales, const uint
 hipError_t launch_gemv_dot(const uint16_t* x, int64_t K, const uint32_t* packed, const uint16_t* scales,
                            const uint16_t* zeros, int64_t N, const int32_t* row_ptr, const int32_t* col,
                            const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
-  const size_t lds = (size_t)16 * (K / 128 + 1) * 4 + (size_t)K * 2;
+  const size_t lds = (size_t)kDotRows * kDotWaves * (K / 128 + 1) * 4 + (size_t)K * 2;
   const int64_t rows_per_block = (int64_t)kDotRows * kDotWaves;
   const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block));
   auto args = [&](auto kern) {
