@@ -101,6 +101,55 @@ __device__ __forceinline__ void lowrank_add32(f32x16 (&acc)[MT][NT], const f16* 
 // BITS = 3: 3-bit codes, 32 per three words (a lane reads one 12-byte run per K
 // step instead of four words); G64: one (s, z) per 64 input channels, which is one
 // per K step.
+// Stores a wave's MT x NT subtiles of 32 x 32 MFMA results (lane 32h + c holds
+// column c of each, value q at row 8 (q / 4) + 4h + q % 4) into out [M, N] (y, or a K
+// slice's fp32 partial), from row mw and column nw. The output kind is chosen by the
+// caller, outside the loops, and a wave whose subtiles lie inside M x N stores with
+// no bounds test: with the kind and the bounds tested per element, the unrolled
+// stores compiled to about a thousand branches per wave, and per-block timestamps put
+// the store of a 128 x 256 prefill tile at 10-19 us.
+template <int MT, int NT, typename T, typename Conv>
+__device__ __forceinline__ void store_subtiles(const f32x16 (&acc)[MT][NT], T* __restrict__ out, int mw, int nw,
+                                               int M, int N, int lane, Conv conv) {
+  const int h = lane >> 5, c = lane & 31;
+  if (mw + 32 * MT <= M && nw + 32 * NT <= N) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        T* p = out + (size_t)(mw + 32 * i + 4 * h) * N + (nw + 32 * j + c);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) p[(size_t)(8 * (q >> 2) + (q & 3)) * N] = conv(acc[i][j][q]);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int n = nw + 32 * j + c;
+        if (n >= N) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = mw + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+          if (m < M) out[(size_t)m * N + n] = conv(acc[i][j][q]);
+        }
+      }
+  }
+}
+
+// y (fp16 or fp32) or the fp32 partial of K slice `slice`, by the kind of output
+template <int MT, int NT>
+__device__ __forceinline__ void store_output(const f32x16 (&acc)[MT][NT], const GemmArgs& a, int slice, int mw,
+                                             int nw, int lane) {
+  const auto same = [](float v) { return v; };
+  if (a.ksplit > 1)
+    store_subtiles<MT, NT>(acc, static_cast<float*>(a.y) + (size_t)slice * a.M * a.N, mw, nw, a.M, a.N, lane, same);
+  else if (a.y_f32)
+    store_subtiles<MT, NT>(acc, static_cast<float*>(a.y), mw, nw, a.M, a.N, lane, same);
+  else
+    store_subtiles<MT, NT>(acc, static_cast<f16*>(a.y), mw, nw, a.M, a.N, lane, [](float v) { return (f16)v; });
+}
+
 template <int BM, int BN, int WGM, int WGN, bool SPARSE, int BITS = 4, bool G64 = false>
 __global__ void __launch_bounds__(64 * WGM * WGN, 2)
 gemm_kernel(GemmArgs a) {
@@ -320,27 +369,7 @@ gemm_kernel(GemmArgs a) {
 
   if (a.lr_r > 0 && slice == 0) lowrank_add32<MT, NT>(acc, a.lr_t, a.lr_up, a.lr_r, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
   // store: the final y, or this slice's fp32 partial tile
-  const bool partial = a.ksplit > 1;
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int n = n0 + wn * WTN + j * 32 + (lane & 31);
-      if (n >= N) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + wm * WTM + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (m < M) {
-          const size_t o = (size_t)m * N + n;
-          if (partial)
-            static_cast<float*>(a.y)[(size_t)slice * M * N + o] = acc[i][j][q];
-          else if (a.y_f32)
-            static_cast<float*>(a.y)[o] = acc[i][j][q];
-          else
-            static_cast<f16*>(a.y)[o] = (f16)acc[i][j][q];
-        }
-      }
-    }
+  store_output<MT, NT>(acc, a, slice, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -613,28 +642,7 @@ gemm_big_kernel(GemmArgs a) {
 
   if (a.lr_r > 0 && slice == 0) lowrank_add32<MT, NT>(acc, a.lr_t, a.lr_up, a.lr_r, M, N, m0 + wm * WTM, n0 + wn * WTN, lane);
   // store: the final y, or this slice's fp32 partial tile
-  const bool partial = a.ksplit > 1;
-  const uint32_t MN = (uint32_t)M * (uint32_t)N;
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int n = n0 + wn * WTN + 32 * j + c32;
-      if (n >= N) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + wm * WTM + 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (m < M) {
-          const uint32_t o = (uint32_t)m * (uint32_t)N + (uint32_t)n;
-          if (partial)
-            static_cast<float*>(a.y)[(size_t)slice * MN + o] = acc[i][j][q];
-          else if (a.y_f32)
-            static_cast<float*>(a.y)[o] = acc[i][j][q];
-          else
-            static_cast<f16*>(a.y)[o] = (f16)acc[i][j][q];
-        }
-      }
-    }
+  store_output<MT, NT>(acc, a, slice, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
 // y = sum over slices s = 0..S-1 of ws[s] (fixed order), in the output dtype.
