@@ -265,31 +265,47 @@ w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, co
   }
 #undef WQ_W8_FETCH
 #undef WQ_W8_STASH
-  // epilogue: s_x of the row, plus the outlier channels' product (one fp16 MFMA)
+  // epilogue: s_x of the row, plus the outlier channels' product (one fp16 MFMA).
+  // The row scales of the lane's 32 rows are loaded together first; the output kind
+  // is chosen once, and a wave inside M x N stores with no bounds test (tested per
+  // element, the kind and the bounds compile to a branch per store).
+  float sxv[2][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const f16x8 ao = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(
-                                                   xo + (size_t)min(m0 + 32 * i + c, M - 1) * kMaxOutliers + 8 * h));
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const f16x8 bo = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(wo + (size_t)col[j] * kMaxOutliers + 8 * h));
-      const f32x16 o = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao, bo, f32x16{}, 0, 0, 0);
-      const int n = n0 + 32 * j + c;
-      if (n >= N) continue;
+    for (int r = 0; r < 16; ++r) sxv[i][r] = sx[min(m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3), M - 1)];
+  const bool full = m0 + 64 <= M && n0 + 64 <= N;
+  const auto epilogue = [&](auto* out, auto conv) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) {
-          const float v = sx[m] * acc[i][j][r] + o[r];
-          const size_t off = (size_t)m * N + n;
-          if (y_f32)
-            static_cast<float*>(y)[off] = v;
-          else
-            static_cast<f16*>(y)[off] = (f16)v;
+    for (int i = 0; i < 2; ++i) {
+      const f16x8 ao = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(
+                                                     xo + (size_t)min(m0 + 32 * i + c, M - 1) * kMaxOutliers + 8 * h));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f16x8 bo =
+            __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(wo + (size_t)col[j] * kMaxOutliers + 8 * h));
+        const f32x16 o = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao, bo, f32x16{}, 0, 0, 0);
+        const int n = n0 + 32 * j + c;
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            out[(size_t)m * N + n] = conv(sxv[i][r] * acc[i][j][r] + o[r]);
+          }
+        } else if (n < N) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (m < M) out[(size_t)m * N + n] = conv(sxv[i][r] * acc[i][j][r] + o[r]);
+          }
         }
       }
     }
-  }
+  };
+  if (y_f32)
+    epilogue(static_cast<float*>(y), [](float v) { return v; });
+  else
+    epilogue(static_cast<f16*>(y), [](float v) { return (f16)v; });
 }
 
 size_t w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
