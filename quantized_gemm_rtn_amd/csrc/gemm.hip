@@ -645,13 +645,34 @@ gemm_big_kernel(GemmArgs a) {
   store_output<MT, NT>(acc, a, slice, m0 + wm * WTM, n0 + wn * WTN, lane);
 }
 
+// sum over slices s = 0..S-1 of ws[s * MN + o], in slice order. The loads go out B at
+// a time (addresses clamped into the S slices, the extra terms added as +0, which
+// leaves the sum unchanged): one load per iteration would wait for each slice in turn.
+// B follows S (2, 4 or 8), so that few slices issue no extra loads.
+template <int B>
+__device__ __forceinline__ float slice_sum_b(const float* __restrict__ ws, int S, size_t MN, size_t o) {
+  float v = 0.f;
+  for (int s0 = 0; s0 < S; s0 += B) {
+    float p[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) p[u] = ws[(size_t)min(s0 + u, S - 1) * MN + o];
+#pragma unroll
+    for (int u = 0; u < B; ++u) v += s0 + u < S ? p[u] : 0.f;
+  }
+  return v;
+}
+__device__ __forceinline__ float slice_sum(const float* __restrict__ ws, int S, size_t MN, size_t o) {
+  if (S <= 2) return slice_sum_b<2>(ws, S, MN, o);
+  if (S <= 4) return slice_sum_b<4>(ws, S, MN, o);
+  return slice_sum_b<8>(ws, S, MN, o);
+}
+
 // y = sum over slices s = 0..S-1 of ws[s] (fixed order), in the output dtype.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ ws, int S, size_t MN, void* __restrict__ y, int y_f32) {
   const size_t stride = (size_t)gridDim.x * 256;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += stride) {
-    float v = ws[i];
-    for (int s = 1; s < S; ++s) v += ws[(size_t)s * MN + i];
+    const float v = slice_sum(ws, S, MN, i);
     if (y_f32)
       static_cast<float*>(y)[i] = v;
     else
@@ -765,8 +786,7 @@ splitk_sparse_reduce_kernel(const float* __restrict__ ws, int S, int M, int N, c
       const int m = mb + ml, n = n0 + nl;
       if (m < M && n < N) {
         const size_t o = (size_t)m * N + n;
-        float v = ws[o];
-        for (int s2 = 1; s2 < S; ++s2) v += ws[(size_t)s2 * MN + o];
+        float v = slice_sum(ws, S, MN, o);
         v += sp[nl][ml];
         if (y_f32)
           static_cast<float*>(y)[o] = v;
