@@ -96,11 +96,6 @@ __device__ __forceinline__ void lowrank_add32(f32x16 (&acc)[MT][NT], const f16* 
   }
 }
 
-// Two waves per SIMD (two blocks per CU): the blocks run out of phase, so one
-// block's waits on memory and barriers are covered by the other's MFMAs.
-// BITS = 3: 3-bit codes, 32 per three words (a lane reads one 12-byte run per K
-// step instead of four words); G64: one (s, z) per 64 input channels, which is one
-// per K step.
 // Stores a wave's MT x NT subtiles of 32 x 32 MFMA results (lane 32h + c holds
 // column c of each, value q at row 8 (q / 4) + 4h + q % 4) into out [M, N] (y, or a K
 // slice's fp32 partial), from row mw and column nw. The output kind is chosen by the
@@ -150,6 +145,11 @@ __device__ __forceinline__ void store_output(const f32x16 (&acc)[MT][NT], const 
     store_subtiles<MT, NT>(acc, static_cast<f16*>(a.y), mw, nw, a.M, a.N, lane, [](float v) { return (f16)v; });
 }
 
+// Two waves per SIMD (two blocks per CU): the blocks run out of phase, so one
+// block's waits on memory and barriers are covered by the other's MFMAs.
+// BITS = 3: 3-bit codes, 32 per three words (a lane reads one 12-byte run per K
+// step instead of four words); G64: one (s, z) per 64 input channels, which is one
+// per K step.
 template <int BM, int BN, int WGM, int WGN, bool SPARSE, int BITS = 4, bool G64 = false>
 __global__ void __launch_bounds__(64 * WGM * WGN, 2)
 gemm_kernel(GemmArgs a) {
