@@ -4,7 +4,7 @@
 // weight, and one (s, z) per 64 input channels (a smaller group than the default,
 // section 5.3 of the same page). Fewer variants are built than for the 4-bit
 // layer: (s, z) staged as vectors of eight halves or by the plain loop, and the
-// block-staged kernel only for 3-bit codes with 128-channel groups.
+// block-staged kernel for one or two rows.
 #include "gemv_kernels.h"
 
 namespace wq {
@@ -18,6 +18,18 @@ static hipError_t launch_lds3(const uint16_t* x, int64_t M, int64_t K, const uin
                      (size_t)2 * G * SR * 4;
   return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, SZV, MR, SP, 3>, lds, 16, x, M, K, packed, scales,
                      zeros, N, row_ptr, col, val, y, y_f32, LowRank{}, stream);
+}
+
+// block-staged activations with one (s, z) per 64 input channels, dequantized into
+// the operand per lane (3- or 4-bit codes)
+template <int XC, int MR, bool SP, int BITS>
+static hipError_t launch_lds_g64(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
+                                 const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
+                                 const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
+  const int64_t Gs = 2 * (K / kGroup), mrows = M < 16 ? M : 16;
+  const size_t lds = (size_t)16 * (Gs + 1) * 4 + (size_t)mrows * K * 2;
+  return launch_rows(gemv_lds_kernel<kGemvWaves, kGemvDepth, XC, 8, MR, SP, BITS, true>, lds, 16, x, M, K, packed,
+                     scales, zeros, N, row_ptr, col, val, y, y_f32, LowRank{}, stream);
 }
 
 template <int XL, int NT, int SZV, bool SP, int BITS, bool G64>
@@ -56,6 +68,21 @@ hipError_t launch_gemv_fmt(const uint16_t* x, int64_t M, int64_t K, const uint32
     WQ_LDS3_X(1) WQ_LDS3_X(2) WQ_LDS3_X(4) WQ_LDS3_X(8) WQ_LDS3_X(16)
 #undef WQ_LDS3_X
 #undef WQ_LDS3
+  }
+  // one or two rows with 64-channel groups: the same staging, (q - z) s per lane
+  if (f.g64 && sv == 8 && mrows_max <= 2 && mrows_max * K <= kXLdsMaxHalves) {
+    const int64_t xloads = (mrows_max * K / 8 + 64 * kGemvWaves - 1) / (64 * kGemvWaves);
+    const int xc = xloads <= 1 ? 1 : xloads <= 2 ? 2 : xloads <= 4 ? 4 : 8;
+    const int mr = mrows_max == 1 ? 1 : 2;
+#define WQ_LG(XC, MR, B)                                      \
+  if (xc == XC && mr == MR && f.bits == B) {                  \
+    if (sp) return launch_lds_g64<XC, MR, true, B>(WQ_ARGS);  \
+    return launch_lds_g64<XC, MR, false, B>(WQ_ARGS);         \
+  }
+#define WQ_LG_X(XC) WQ_LG(XC, 1, 4) WQ_LG(XC, 2, 4) WQ_LG(XC, 1, 3) WQ_LG(XC, 2, 3)
+    WQ_LG_X(1) WQ_LG_X(2) WQ_LG_X(4) WQ_LG_X(8)
+#undef WQ_LG_X
+#undef WQ_LG
   }
   const int xl = mrows_max <= 4 ? 1 : (mrows_max <= 8 ? 2 : 4);
   const int64_t pairs = ((N + 31) / 32) * ((M + 15) / 16);

@@ -370,7 +370,11 @@ __device__ __forceinline__ void lowrank_add16(f32x4 (&acc)[NT], const LrFirst<NT
   }
 }
 
-template <int KW, int D, int XC, int SZV, int MR, bool SP, int BITS = 4>
+// G64: one (s, z) per 64 input channels. A lane's 32 channels of a group lie in one
+// half of it, so each lane dequantizes (q - z) s into the operand with its own (s, z)
+// (the 128-channel correction per group below cannot split the two halves): the
+// activations are staged unscaled and without the sum tables, and (s, z) in LDS.
+template <int KW, int D, int XC, int SZV, int MR, bool SP, int BITS = 4, bool G64 = false>
 __global__ void __launch_bounds__(64 * KW)
 gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
                 const f16* __restrict__ scales, const f16* __restrict__ zeros, int N,
@@ -385,13 +389,15 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform, in a scalar register
   const int r = lane & 15, h = lane >> 4;
   const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  static_assert(!G64 || SZV != kSzInRegs, "64-channel groups stage (s, z) in LDS");
   const int G = K >> 7;
+  const int Gs = G64 ? 2 * G : G;  // (s, z) per row
   const int mrows = min(16, M - m0);
   const int SR = MR == 1 ? 1 : 4 * ((mrows + 3) >> 2);  // rows of the x-sum tables
   // LDS: sz[16][G + 1] (s, 1024 + z), unless SZV == kSzInRegs |
   //      xs[mrows][K] permuted, odd channels / 16 |
   //      sums of x over even / odd channels per (group, row)
-  const size_t sz_bytes = SZV == kSzInRegs ? 0 : (size_t)16 * (G + 1) * 4;
+  const size_t sz_bytes = SZV == kSzInRegs ? 0 : (size_t)16 * (Gs + 1) * 4;
   f16x2* sz = reinterpret_cast<f16x2*>(smem);
   f16* xs = reinterpret_cast<f16*>(smem + sz_bytes);
   // x sums per group: [g][2][SR] (even rows then odd rows); with MR == 1, SR == 1
@@ -413,7 +419,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
     sp_e1 = row_ptr[n_ld + 1];
   }
   SzStage<SZV == kSzInRegs ? 8 : SZV, T> szs;
-  if constexpr (SZV != kSzInRegs) szs.load(scales, zeros, n0, N, G, t);
+  if constexpr (SZV != kSzInRegs) szs.load(scales, zeros, n0, N, Gs, t);
   // the block's rows of x are contiguous in memory and in LDS
   const int x_vecs = mrows * (K >> 3);
   const f16* xblk = x + (size_t)m0 * K;
@@ -449,7 +455,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   for (int i = 0; i < D0; ++i) prefetch(i);
   __builtin_amdgcn_sched_barrier(0);
 
-  if constexpr (SZV != kSzInRegs) szs.store(sz, scales, zeros, n0, N, G, t);
+  if constexpr (SZV != kSzInRegs) szs.store(sz, scales, zeros, n0, N, Gs, t);
   const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
   const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 #pragma unroll
@@ -463,7 +469,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
     float so = __builtin_amdgcn_fdot2(as_f16x2(p.y), ones, 0.0f, false);
     so = __builtin_amdgcn_fdot2(as_f16x2(p.w), ones, so, false);
     uint4 q = p;
-    if constexpr (BITS == 4) {  // odd positions meet codes carrying a factor 16
+    if constexpr (BITS == 4 && !G64) {  // odd positions meet codes carrying a factor 16
       q.y = as_u32(as_f16x2(p.y) * sixteenth);
       q.w = as_u32(as_f16x2(p.w) * sixteenth);
     }
@@ -473,7 +479,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
     // the 16 chunks of a group sit in one 16-lane row; its total lands in lane 15
     se = row16_sum_to_last(se);
     so = row16_sum_to_last(so);
-    if ((idx_raw & 15) == 15 && idx_raw < x_vecs) {
+    if (!G64 && (idx_raw & 15) == 15 && idx_raw < x_vecs) {
       if constexpr (MR == 1) {  // a single row
         const int g = idx_raw >> 4;
         sab[2 * g] = se;
@@ -497,7 +503,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   // ---- main loop over this wave's groups
   const int xr = min(r, mrows - 1);
   const f16* xl = xs + (size_t)xr * K + 32 * h;
-  const f16x2* szr = sz + r * (G + 1);
+  const f16x2* szr = sz + r * (Gs + 1);
   const int srow = min(4 * h, SR - 4);
   const uint32_t magic = magic_1024x2();
 
@@ -510,6 +516,21 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
     for (int tt = 0; tt < 4; ++tt) xa[tt] = *reinterpret_cast<const uint4*>(xl + (size_t)g * 128 + 8 * tt);
     __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // DS reads first
     f32x4 part = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (G64) {
+      // lanes h = 0, 1 and h = 2, 3 fall in the two halves of the group
+      const f16x2 sbz = szr[2 * g + (h >> 1)];
+      const f16x2 bias = {sbz[1], sbz[1]};
+      const f16 nb = (f16)960.0f - sbz[1];  // -(64 + z)
+      const f16x2 nbias16 = {nb, nb};
+      const f16x2 s2 = {sbz[0], sbz[0]};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        part = mfma_16x16x32(as_f16x8(xa[tt]), as_f16x8(step_operand<true>(w, tt, magic, bias, nbias16, s2)), part);
+#pragma unroll
+      for (int i = 0; i < MR; ++i) acc[i] += part[i];
+      hold_accumulator(part, acc);
+      return;
+    }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
       part = mfma_16x16x32(as_f16x8(xa[tt]), as_f16x8(step_biased(w, tt, magic)), part);
@@ -581,7 +602,7 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
   if constexpr (SP) {
     const auto add = [&](int c, float v) {
       const int cs = (c & ~7) | perm_slot(c & 7);
-      const float vu = BITS == 4 && (c & 1) ? 16.0f * v : v;  // odd channels were stored / 16
+      const float vu = BITS == 4 && !G64 && (c & 1) ? 16.0f * v : v;  // odd channels were stored / 16
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = min(4 * h + i, mrows - 1);
