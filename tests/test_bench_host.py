@@ -38,3 +38,14 @@ def test_cpu_baseline_record():
     assert b["value"] > 0 and b["cores"] >= 1
     assert set(b["phases_ms"]) == {"quantize_fp32", "dequantize_fp64", "linear_ref"}
     assert "11008" in b["sample"] and "4096" in b["sample"]
+
+
+def test_traffic_record_describes_the_current_decode_kernel():
+    """The committed HBM-traffic record of the headline's decode kernel (which the
+    bench reports as roofline.traffic) was measured on the kernel's current sources:
+    a change to them needs the counters taken again."""
+    t = bench.recorded_traffic()
+    assert t is not None, "profiles/gemv_decode_7b_up_proj_traffic.txt describes other kernel sources"
+    # within a few percent of the algorithmic bytes: every weight read from HBM once
+    alg = bench.alg_bytes(1, 11008, 4096, 0)
+    assert 0.99 * alg <= t <= 1.05 * alg
