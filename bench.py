@@ -268,6 +268,32 @@ def stream_copy(torch, nbytes, steps=100):
             "GBps_read_plus_write": 2 * n * 4 / (us * 1e-6) / 1e9}
 
 
+def device_context(torch):
+    """The GPU's own figures, to check the public ones the rooflines use (256 CUs,
+    2.4 GHz peak engine clock, 160 KB of LDS per CU): torch's device properties,
+    and the peak clock and compute units that rocminfo reports for the agent."""
+    import re
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    d = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+         "total_memory_GiB": round(p.total_memory / 2**30, 1), "l2_cache_bytes": getattr(p, "L2_cache_size", None),
+         "wave_size": getattr(p, "warp_size", None)}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        arch = d["gcn_arch"].split(":")[0]
+        for block in out.split("*******"):
+            if arch and re.search(r"^\s*Name:\s+" + re.escape(arch) + r"\s*$", block, re.M):
+                for line in block.splitlines():
+                    if "Max Clock Freq. (MHz):" in line:
+                        d["rocminfo_max_clock_mhz"] = int(line.split(":")[1].split()[0])
+                    if line.strip().startswith("Compute Unit:"):
+                        d["rocminfo_compute_units"] = int(line.split(":")[1].split()[0])
+                break
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    return d
+
+
 def stream_read(torch, nbytes, steps=200):
     """Context for the decode rows: one launch of a plain streaming-read kernel
     (libwq_probe.so) over nbytes, rotating over >= 1 GiB of sources, timed like the
@@ -509,10 +535,12 @@ def main():
 
     context = None
     if not args.quick:
-        context = {"stream_read_headline_bytes": stream_read(torch, alg_bytes(1, 11008, 4096, 0)),
+        context = {"device": device_context(torch),
+                   "stream_read_headline_bytes": stream_read(torch, alg_bytes(1, 11008, 4096, 0)),
                    "stream_read_70b_m1_bytes": stream_read(torch, alg_bytes(1, 8192, 28672, 117440)),
                    "torch_copy_headline_bytes": stream_copy(torch, alg_bytes(1, 11008, 4096, 0)),
                    "torch_copy_256MiB": stream_copy(torch, 256 << 20, steps=20)}
+        print(f"# device (context): {context['device']}", file=sys.stderr, flush=True)
         for k in ("stream_read_headline_bytes", "stream_read_70b_m1_bytes"):
             c = context[k]
             print(f"# {k} (context): {c['us_per_launch']:.2f} us  {c['GBps']:.1f} GB/s "
