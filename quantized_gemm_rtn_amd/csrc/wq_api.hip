@@ -210,8 +210,8 @@ size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // The decode kernels re-read the weights once per 16 rows, the GEMM reads them once
 // but needs a grid that fills the GPU. Measured on the 4096 x 4096 layer with its
 // CSR (the GEMM splits K at most twice there: 32 blocks), the decode kernel stays
-// faster up to M = 64 (25.8 against 35.1 us); on the 8192 x 28672 layer (256
-// blocks) the GEMM takes over from M = 20 (67.5 against 76.6 us).
+// faster up to M = 64 (25.8 against 28.1 us); on the 8192 x 28672 layer (256
+// blocks) the GEMM takes over from M = 20 (64.1 against 77.3 us).
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K) {
   if (M <= 16) return WQ_KERNEL_GEMV;
   if (M <= 64 && N >= 1 && K >= kGroup && K % kGroup == 0 && wq::gemm_grid_blocks(M, N, K) < 128)
