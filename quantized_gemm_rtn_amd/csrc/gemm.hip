@@ -70,6 +70,9 @@ struct GemmArgs {
   const f16* lr_t;
   const f16* lr_up;
   int lr_r;
+  // x^T [K][xt_mp] for a sparse term added in the slice sum (gemm_big_kernel<..., true>)
+  f16* xt;
+  int xt_mp;
 };
 
 // Up-projection of a low-rank branch for a wave's MT x NT subtiles of 32 x 32:
@@ -374,6 +377,7 @@ gemm_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 constexpr int kBigSS = 128;                // halves per super-step (one group)
+constexpr int kXtPerThread = 2;            // transpose items per thread and super-step (XT)
 constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 groups x 256 columns
 
 // Dense kernel for large M. As launched: block tile 128 x 256, four waves side by
@@ -394,7 +398,12 @@ constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 gro
 //    sub-step ks it feeds the eight input channels 64 (ks / 4) + 32h + 8 (ks % 4)
 //    of the group (word 8 (ks / 4) + 4h + ks % 4 of the column's 16 words), in
 //    their natural order, matching activations kept in natural order in LDS.
-template <int BM, int BN, int WGM, int WGN, int MINB, int WS>
+//  - With XT, the block also writes its share of the activations' transpose
+//    xt [K][Mp] (Mp: M rounded up to 8, rows M .. Mp - 1 zero) from the LDS stage of
+//    each super-step: 128 / tiles_n (rounded up) input channels of the group for the
+//    block's rows, so that the tiles_n blocks of a row tile and slice cover every
+//    channel once. The slice sum then gathers the sparse term's activations from it.
+template <int BM, int BN, int WGM, int WGN, int MINB, int WS, bool XT>
 __global__ void __launch_bounds__(64 * WGM * WGN, MINB)
 gemm_big_kernel(GemmArgs a) {
   constexpr int T = 64 * WGM * WGN;
@@ -425,6 +434,7 @@ gemm_big_kernel(GemmArgs a) {
   const int slice = bid / ntile;
   const int tile = bid - slice * ntile;
   const int m0 = (tile % a.tiles_m) * BM, n0 = (tile / a.tiles_m) * BN;
+  const int tn = tile / a.tiles_m;
   // (block-uniform values, kept in scalar registers for the loads' scalar offsets)
   const int g0 = __builtin_amdgcn_readfirstlane(slice * (a.k_per_slice >> 7));            // even
   const int ng = __builtin_amdgcn_readfirstlane(min(G, g0 + (a.k_per_slice >> 7)) - g0);  // even
@@ -523,6 +533,44 @@ gemm_big_kernel(GemmArgs a) {
     for (int j = 0; j < NT; ++j) sz[j] = szl[(2 * buf + grp) * 256 + wn * WTN + 32 * j + c32];
   };
   const uint32_t magic = magic_1024x2();
+  // Transpose items of this thread (XT): the LDS offset of its value in a stage, its
+  // byte offset in xt without the group's part (past the end when the item is not this
+  // block's, so that the buffer store writes nothing), and whether its row is past M.
+  // The block's items: cpb = 128 / tiles_n (rounded up) channels from tn cpb, those
+  // below 128, times its rows below Mp; the launcher sends only shapes with
+  // cpb BM <= kXtPerThread T, so a fixed number of items per thread covers them (no
+  // loop, which would split the unrolled super-step).
+  uint32_t xt_lds[kXtPerThread], xt_off[kXtPerThread];
+  bool xt_zero[kXtPerThread];
+  const __amdgpu_buffer_rsrc_t xtrs = buffer_rsrc(a.xt, XT ? (uint32_t)K * (uint32_t)a.xt_mp * 2u : 0u);
+  if constexpr (XT) {
+    const int cpb = (kBigSS + a.tiles_n - 1) / a.tiles_n;
+#pragma unroll
+    for (int i = 0; i < kXtPerThread; ++i) {
+      const int q = t + i * T;
+      const int cl = q / BM, r = q - cl * BM;
+      const int ch = tn * cpb + cl, m = m0 + r;
+      const bool mine = cl < cpb && ch < kBigSS && m < a.xt_mp;
+      xt_lds[i] = (uint32_t)(r * kBigSS + ((((ch >> 3) & 15) ^ (r & 15)) << 3) + (ch & 7));
+      xt_off[i] = mine ? ((uint32_t)ch * (uint32_t)a.xt_mp + (uint32_t)m) * 2u : 0x80000000u;
+      xt_zero[i] = m >= M;
+    }
+  }
+  // xt[g0 + g][ch][m] for the thread's items from stage xs (the swizzled layout above),
+  // 64 consecutive rows per wave at 64-row tiles. Issued at the start of the super-step,
+  // before its loads: the barrier's counted wait then still leaves only weight loads in
+  // flight, whatever order loads and stores complete in. (Stored at the end of the
+  // super-step instead, after the loads, the 70B layer at M = 512 took 1.2 us less,
+  // but the wait would rely on stores being counted off in order with loads.)
+  auto write_xt = [&](const f16* xs, int g) {
+    const int so = __builtin_amdgcn_readfirstlane((g0 + g) * kBigSS * a.xt_mp * 2);
+#pragma unroll
+    for (int i = 0; i < kXtPerThread; ++i) {
+      const f16 v = xs[xt_lds[i]];
+      const unsigned short b = xt_zero[i] ? (unsigned short)0 : __builtin_bit_cast(unsigned short, v);
+      __builtin_amdgcn_raw_buffer_store_b16(b, xtrs, (int)xt_off[i], so, 0);
+    }
+  };
   // A fragment of row r, chunk c = 8 (ks / 4) + 4h + ks % 4 (r & 15 == c32 & 15)
   auto read_a = [&](f16x8 (&av)[MT], const f16* xs, int ks) {
     const int c = (8 * (ks >> 2) + 4 * h + (ks & 3)) ^ (c32 & 15);
@@ -571,7 +619,10 @@ gemm_big_kernel(GemmArgs a) {
       f16x8 (&cur)[MT] = (ks & 1) ? a1 : a0;
       f16x8 (&nxt)[MT] = (ks & 1) ? a0 : a1;
       // (s, z) and activation loads first, weight loads after them: the barrier at the
-      // end then waits for the activations only
+      // end then waits for the activations only (the transpose's stores, older still,
+      // with them)
+      if constexpr (XT)
+        if (ks == 0) write_xt(xs, g);
       if (ks == 0 && pp == 1) load_sz(g + 3);
       if (ks == 0) {
 #pragma unroll
@@ -597,6 +648,7 @@ gemm_big_kernel(GemmArgs a) {
         for (int i = 0; i < MT; ++i) acc[i][j] = mfma_32x32x16(cur[i], bcur, acc[i][j]);
         bcur = bnext;
       }
+
       // (two waves per SIMD interleave MFMAs and vector work by themselves; an
       // explicit per-MFMA interleaving here only cost registers)
       __builtin_amdgcn_sched_barrier(0);
@@ -886,7 +938,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 template <int BM, int BN, int WGM, int WGN, int MINB, int WS>
 static hipError_t launch_big(GemmArgs a, hipStream_t stream) {
   constexpr size_t lds = 2 * (size_t)BM * kBigSS * sizeof(f16) + kBigSzBytes;
-  auto kern = gemm_big_kernel<BM, BN, WGM, WGN, MINB, WS>;
+  auto kern = a.xt != nullptr ? gemm_big_kernel<BM, BN, WGM, WGN, MINB, WS, true>
+                              : gemm_big_kernel<BM, BN, WGM, WGN, MINB, WS, false>;
   {
     const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
@@ -947,7 +1000,11 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     f16* xt = p.sparse_in_reduce
                   ? reinterpret_cast<f16*>(static_cast<char*>(workspace) + partials_bytes(p, mc, N))
                   : nullptr;
-    if (p.sparse_in_reduce) {
+    // the GEMM writes x^T itself when its blocks' shares fit (wide layers); else a launch
+    const int64_t big_bm = p.kind == 1 ? 128 : 64, tn = (N + 255) / 256;
+    const bool xt_in_gemm = p.sparse_in_reduce && (kBigSS + tn - 1) / tn * big_bm <= kXtPerThread * 256 &&
+                            (size_t)K * (size_t)Mp * 2 < ((size_t)1 << 31);
+    if (p.sparse_in_reduce && !xt_in_gemm) {
       const dim3 tgrid((unsigned)(K / 64), (unsigned)((mc + 63) / 64));
       hipLaunchKernelGGL(transpose_x_kernel, tgrid, dim3(256), 0, stream, reinterpret_cast<const f16*>(x) + m * K,
                          (int)mc, (int)K, xt, (int)Mp);
@@ -975,6 +1032,8 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.lr_t = lr.r > 0 ? reinterpret_cast<const f16*>(lr.t) + m * lr.r : nullptr;
     a.lr_up = reinterpret_cast<const f16*>(lr.up);
     a.lr_r = (int)lr.r;
+    a.xt = xt_in_gemm ? xt : nullptr;  // written by gemm_big_kernel<..., true>
+    a.xt_mp = (int)Mp;
     hipError_t e;
     // weight windows of WS super-steps need slices and K of a multiple of 2 WS groups;
     // kind 2 has G and its slices (or the whole K) multiples of four groups, so WS is

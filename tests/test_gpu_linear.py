@@ -187,7 +187,24 @@ def test_sparse_large_m_split(gpu_lib, M, N, K):
     _full_check(gpu_lib, torch, L, x, "gemm", label="sparse split")
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 96, 4096), (200, 256, 4096), (520, 300, 2048)])
+@pytest.mark.parametrize("M,N,K", [(37, 11008, 4096), (5, 8192, 4096), (48, 8192, 3072), (64, 3841, 2048),
+                                   (64, 3840, 2048), (130, 16384, 2048), (300, 8192, 2048)])
+def test_sparse_split_wide_layers(gpu_lib, M, N, K):
+    """CSR products on layers wide enough (at least 16 column tiles of 64-row tiles,
+    32 of 128-row tiles) that the split GEMM writes the transposed activations
+    itself, each block a share of every group's channels: ragged M (rows past M
+    written as zero), 43 column tiles (shares of 3 channels, the last one partly past
+    the group), both tile heights, weight windows of two and four groups, and 3840
+    output channels, the widest 64-row layer that still takes the transpose launch."""
+    import torch
+    W = workloads.random_weights(3 * M + N + K, N, K)
+    L = oracle.quantize_layer(W, N * K // 200)
+    x = workloads.random_x(M + 23, M, K)
+    _full_check(gpu_lib, torch, L, x, "gemm", label="sparse split, wide")
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 96, 4096), (200, 256, 4096), (520, 300, 2048), (37, 11008, 2048),
+                                   (300, 8192, 2048)])
 def test_integer_exact_fp32_sparse_split(gpu_lib, M, N, K):
     """The integer-exact case with a CSR term through the split dense kernels."""
     import torch
