@@ -66,7 +66,8 @@ def alg_flops(M, N, K, nnz, rank=0):
 class Layer:
     """A quantized layer on the GPU, produced by the library's own quantizer."""
 
-    def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False, w4a8=False, bits=4, group=128):
+    def __init__(self, wq, torch, index, M, K=None, rank=0, act_order=False, w4a8=False, bits=4, group=128,
+                 sparse_ppm=None):
         W, x, cfg = workloads.make(index, M=M, K=K)
         N, K = W.shape
         self.wq = wq
@@ -76,6 +77,8 @@ class Layer:
             self.outliers = torch.from_numpy(workloads.x_outlier_channels(index, M=M, K=K)).cuda()
             self.ws_bytes = wq.linear_w4a8_workspace_bytes(M, N, K)
         self.sparse_k = workloads.sparse_k_for(cfg, N, K)
+        if sparse_ppm is not None:
+            self.sparse_k = sparse_ppm * N * K // 1_000_000
         Wd = torch.from_numpy(W).cuda()
         if act_order:
             self.perm = torch.from_numpy(workloads.channel_permutation(index + 7, K)).cuda()
@@ -216,11 +219,14 @@ def measure(wq, torch, index, M, steps, warmup, kernel="auto", K=None, replays=5
     permuted channel order, x gathered through the permutation; mode "w8": the
     W4A8 product with the configuration's activation outlier channels in fp16
     (the layer has no CSR then); mode "b3": 3-bit codes in the 3-bit packing;
-    "g64": one (s, z) per 64 input channels; "b3g64": both."""
+    "g64": one (s, z) per 64 input channels; "b3g64": both; "sp": the layer's
+    outliers at 0.45 % of the weights (the batched-decode layer's density), also
+    where the configuration has none (the prefill layer)."""
     act_order, w4a8 = mode == "ao", mode == "w8"
     bits = 3 if mode in ("b3", "b3g64") else 4
     group = 64 if mode in ("g64", "b3g64") else 128
-    L = Layer(wq, torch, index, M, K, rank, act_order, w4a8, bits, group)
+    L = Layer(wq, torch, index, M, K, rank, act_order, w4a8, bits, group,
+              sparse_ppm=workloads.SPARSE_PPM_DENSE_AND_SPARSE if mode == "sp" else None)
     if w4a8:
         L.sparse_k = 0
     sets = L.sets(torch, ROTATE_BYTES)
@@ -513,6 +519,9 @@ def main():
                      (2, 1, "auto", None, 0, "ao"), (4, 2048, "auto", None, 0, "ao")]
             # the prefill layer as a W4A8 product with its 8 fp16 outlier channels
             plan += [(4, 2048, "auto", None, 0, "w8")]
+            # the prefill layer and the 70B layer at M = 512 with CSR outliers at 0.45 %
+            # of the weights (the dense-and-sparse prefill)
+            plan += [(4, 2048, "auto", None, 0, "sp"), (5, 512, "auto", None, 0, "sp")]
             # the decode layers with 3-bit codes and with 64-channel groups
             plan += [(2, 1, "auto", None, 0, "b3"), (2, 1, "auto", None, 0, "g64"), (2, 1, "auto", None, 0, "b3g64"),
                      (5, 8, "auto", None, 0, "b3"), (4, 2048, "auto", None, 0, "b3")]
@@ -522,7 +531,7 @@ def main():
             rows.append(r)
             print(f"# {r['config']}:{r['M']}{'' if Kov is None else ' K=%d' % Kov}{' r=%d' % rank if rank else ''}"
                   f"{' act-order' if mode == 'ao' else ''}{' w4a8' if mode == 'w8' else ''}"
-                  f"{' ' + mode if mode in ('b3', 'g64', 'b3g64') else ''} "
+                  f"{' ' + mode if mode in ('b3', 'g64', 'b3g64', 'sp') else ''} "
                   f"{r['kernel']:4s} "
                   f"{r['us_per_launch']:9.2f} us  "
                   f"{r['GBps']:8.1f} GB/s ({100 * r['hbm_frac']:5.1f}%)  {r['TFLOPs']:7.1f} TF/s "

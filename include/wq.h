@@ -157,8 +157,9 @@ int wq_pack_bits(const uint8_t* codes, int64_t N, int64_t K, int32_t bits, uint3
  * dimension of the prefill GEMM across blocks (fp32 partial sums, reduced in a
  * fixed order), for shapes whose output tiles alone cannot fill the GPU, and, for a
  * product with a CSR term, hold the activations transposed ([K, M rounded up to 8]
- * fp16) so that the sparse term joins that fixed-order sum. 0 when no split is
- * planned. A call given less (or NULL) runs unsplit: same results up to rounding
+ * fp16) and, when K is not split, one fp32 partial of y, so that the sparse term
+ * joins that fixed-order sum. 0 when neither is planned. A call given less (or
+ * NULL) runs unsplit, the sparse term inside the GEMM: same results up to rounding
  * order, slower. */
 size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -228,13 +229,14 @@ int wq_linear_sparse_kernel(const uint16_t* x, int64_t M, int64_t K,
  * wq_linear_sparse_noalloc - wq_linear_sparse (kernel chosen by M; row_ptr may be
  * NULL when nnz == 0, the dense product) for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc. It takes no workspace and allocates nothing: the split-K partial sums
+ * hipMalloc. It takes no workspace and allocates nothing: the fp32 partial sums
  * and transposed activations of the GEMM go to a scratch array of
  * WQ_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory from the
  * first such call on that GPU (the current device) until the process ends.
- *  - A product that would need more (wq_linear_workspace_bytes(M, N, K) above
- *    WQ_NOALLOC_SCRATCH_BYTES on the GEMM path) returns WQ_ERR_SCRATCH and
- *    launches nothing.
+ *  - A product whose GEMM plan would need more (its split-K partial sums; with a
+ *    CSR term also the transposed activations and, when K is not split, one fp32
+ *    partial of y; at most wq_linear_workspace_bytes(M, N, K)) returns
+ *    WQ_ERR_SCRATCH and launches nothing.
  *  - Every call on one GPU uses the same scratch: calls that can run at the same
  *    time on one GPU (other streams, other host threads) race and give wrong
  *    results. Queue them on one stream, or use wq_linear_sparse with separate

@@ -856,8 +856,8 @@ struct GemmPlan {
   // with weight windows of four or two super-steps
   int kind;
   int ksplit, k_per_slice;
-  // the sparse term is added in the slice sum, from activations transposed into the
-  // workspace, instead of inside gemm_kernel
+  // the sparse term is added in the slice sum (of one slice or several), from
+  // activations transposed into the workspace, instead of inside gemm_kernel
   bool sparse_in_reduce;
 };
 
@@ -897,7 +897,7 @@ static GemmPlan plan_gemm_kind(int64_t M, int64_t N, int64_t K, bool sparse) {
 }
 
 static size_t partials_bytes(const GemmPlan& p, int64_t M, int64_t N) {
-  return p.ksplit > 1 ? ((size_t)p.ksplit * M * N * 4 + 255) / 256 * 256 : 0;
+  return p.ksplit > 1 || p.sparse_in_reduce ? ((size_t)p.ksplit * M * N * 4 + 255) / 256 * 256 : 0;
 }
 
 static int64_t padded_rows(int64_t M) { return (M + 7) / 8 * 8; }
@@ -906,12 +906,13 @@ static size_t plan_workspace(const GemmPlan& p, int64_t M, int64_t N, int64_t K)
   return partials_bytes(p, M, N) + (p.sparse_in_reduce ? (size_t)K * padded_rows(M) * 2 : 0);
 }
 
-// A product with a CSR term takes the dense kernel of its shape when that kernel
-// splits K: the sparse term then joins the slice sum.
+// A product with a CSR term takes the dense kernel of its shape when that is
+// gemm_big_kernel, split or not: the sparse term then joins the slice sum (of one
+// fp32 slice when K is not split). Other shapes take gemm_kernel, the term inside.
 static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
   if (sparse) {
     GemmPlan d = plan_gemm_kind(M, N, K, false);
-    if (d.kind != 0 && d.ksplit > 1) {
+    if (d.kind != 0) {
       d.sparse_in_reduce = true;
       return d;
     }
@@ -933,6 +934,12 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const size_t b = plan_workspace(plan_gemm(M, N, K, true), M, N, K);
   const size_t c = plan_workspace(plan_gemm_kind(M, N, K, true), M, N, K);
   return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
+
+// the workspace of the plan a 4-bit, 128-channel-group product of this shape takes
+// with a full workspace, dense or with a CSR term
+size_t gemm_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sparse) {
+  return plan_workspace(plan_gemm(M, N, K, sparse), M, N, K);
 }
 
 template <int BM, int BN, int WGM, int WGN, int MINB, int WS>
@@ -1022,11 +1029,11 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     a.val = reinterpret_cast<const f16*>(val);
     a.nnz = sp_kernel ? nnz : 0;
     void* yout = static_cast<char*>(y) + (size_t)(m * N) * ysz;
-    a.y = p.ksplit > 1 ? workspace : yout;
+    a.y = p.ksplit > 1 || p.sparse_in_reduce ? workspace : yout;
     a.M = (int)mc;
     a.N = (int)N;
     a.K = (int)K;
-    a.y_f32 = y_f32;
+    a.y_f32 = p.sparse_in_reduce ? 1 : y_f32;  // one fp32 slice when not split
     a.ksplit = p.ksplit;
     a.k_per_slice = p.k_per_slice;
     a.lr_t = lr.r > 0 ? reinterpret_cast<const f16*>(lr.t) + m * lr.r : nullptr;

@@ -314,7 +314,7 @@ int wq_linear_sparse_noalloc(const uint16_t* x, int64_t M, int64_t K, const uint
   if (rc != WQ_OK) return rc;
   if (M == 0) return WQ_OK;
   const int kernel = wq_auto_kernel(M, N, K);
-  const size_t need = kernel == WQ_KERNEL_GEMM ? wq::gemm_workspace_bytes(M, N, K) : 0;
+  const size_t need = kernel == WQ_KERNEL_GEMM ? wq::gemm_plan_workspace_bytes(M, N, K, nnz > 0) : 0;
   if (need > WQ_NOALLOC_SCRATCH_BYTES) return WQ_ERR_SCRATCH;
   const int y_f32 = y_dtype == WQ_F32;
   const int32_t* rp = nnz > 0 ? row_ptr : nullptr;

@@ -92,6 +92,9 @@ hipError_t launch_pack3(const uint8_t* codes, int64_t N, int64_t K, uint32_t* pa
 // cannot fill the GPU and the workspace holds gemm_workspace_bytes(M, N, K);
 // otherwise it runs unsplit.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// ... of the plan one product takes (4-bit codes, 128-channel groups; a CSR term or
+// not); at most gemm_workspace_bytes(M, N, K)
+size_t gemm_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sparse);
 // blocks of the dense GEMM's launch for M x N x K (split K included)
 int64_t gemm_grid_blocks(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,

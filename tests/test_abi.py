@@ -72,8 +72,12 @@ def test_workspace_sizes(lib):
     b = lib.wq_quantize_workspace_bytes(4096, 4096, 75497)
     assert b >= 4096 * 4096 // 8 + 3 * 4096 * 4 + 2048 * 4
     assert lib.wq_quantize_workspace_bytes(64, 100, 5) == 0      # invalid K
-    # the prefill GEMM splits K only when its tile grid cannot fill the GPU
-    assert lib.wq_linear_workspace_bytes(2048, 14336, 4096) == 0
+    # the prefill GEMM splits K only when its tile grid cannot fill the GPU; a CSR
+    # product of that shape still needs one fp32 partial of y and x transposed
+    assert lib.wq_linear_workspace_bytes(2048, 14336, 4096) == 2048 * 14336 * 4 + 4096 * 2048 * 2
+    # shapes that only the tile kernel takes (K not a multiple of four groups at
+    # M <= 64, an odd number of groups above 128 rows) need nothing unsplit
+    assert lib.wq_linear_workspace_bytes(40, 8192, 3 * 128) == 0
     # split-K partials, plus the transposed activations of a product with a CSR term
     ws = lib.wq_linear_workspace_bytes(512, 8192, 28672)
     assert ws >= 2 * 512 * 8192 * 4 + 28672 * 512 * 2
@@ -311,3 +315,8 @@ def test_noalloc_validation(lib):
     assert f(A, M, K, A2, A3, A4, N, 128, A, A2, A3, 10, A5, 0, None) == -7
     # the 70B down-projection at M = 512 with its CSR fits (about 92 MiB)
     assert lib.wq_linear_workspace_bytes(512, 8192, 28672) <= 96 << 20
+    # the prefill layer with a CSR term does not split K: one fp32 partial of y and
+    # the transposed activations (134 MB) exceed the scratch
+    M, N, K = 2048, 14336, 4096
+    assert lib.wq_linear_workspace_bytes(M, N, K) == M * N * 4 + K * M * 2
+    assert f(A, M, K, A2, A3, A4, N, 128, A, A2, A3, 10, A5, 0, None) == -7

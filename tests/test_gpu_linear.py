@@ -62,6 +62,19 @@ def test_config4_prefill_all_outputs(gpu_lib):
     _all_rows_check(gpu_lib, torch, L, x, "auto", "config 4")
 
 
+def test_config4_prefill_with_csr_all_outputs(gpu_lib):
+    """The prefill layer with CSR outliers at 0.45 % of its weights (264 241
+    entries), as the bench times it: the 128 x 256 GEMM unsplit, writing one fp32
+    partial and the transposed activations, then the slice sum with the sparse
+    term; every output compared."""
+    import torch
+    W, x, _ = workloads.make(4)
+    N, K = W.shape
+    L = oracle.quantize_layer(W, workloads.SPARSE_PPM_DENSE_AND_SPARSE * N * K // 1_000_000)
+    del W, L["W_dense"]
+    _all_rows_check(gpu_lib, torch, L, x, "auto", "config 4 + CSR")
+
+
 @pytest.mark.parametrize("M", [1, 8, 64, 512])
 def test_config5_sweep_all_outputs(gpu_lib, M):
     import torch
@@ -188,14 +201,17 @@ def test_sparse_large_m_split(gpu_lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(37, 11008, 4096), (5, 8192, 4096), (48, 8192, 3072), (64, 3841, 2048),
-                                   (64, 3840, 2048), (130, 16384, 2048), (300, 8192, 2048)])
+                                   (64, 3840, 2048), (130, 16384, 2048), (300, 8192, 2048), (300, 2048, 1024),
+                                   (1100, 8192, 1024), (40, 1000, 1024), (40, 8192, 1024)])
 def test_sparse_split_wide_layers(gpu_lib, M, N, K):
     """CSR products on layers wide enough (at least 16 column tiles of 64-row tiles,
     32 of 128-row tiles) that the split GEMM writes the transposed activations
     itself, each block a share of every group's channels: ragged M (rows past M
     written as zero), 43 column tiles (shares of 3 channels, the last one partly past
     the group), both tile heights, weight windows of two and four groups, and 3840
-    output channels, the widest 64-row layer that still takes the transpose launch."""
+    output channels, the widest 64-row layer that still takes the transpose launch;
+    and products whose GEMM does not split K (one fp32 slice, then the same sum), on
+    wide and narrow layers of both tile heights."""
     import torch
     W = workloads.random_weights(3 * M + N + K, N, K)
     L = oracle.quantize_layer(W, N * K // 200)
@@ -204,7 +220,7 @@ def test_sparse_split_wide_layers(gpu_lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(40, 96, 4096), (200, 256, 4096), (520, 300, 2048), (37, 11008, 2048),
-                                   (300, 8192, 2048)])
+                                   (300, 8192, 2048), (300, 2048, 1024), (40, 8192, 1024)])
 def test_integer_exact_fp32_sparse_split(gpu_lib, M, N, K):
     """The integer-exact case with a CSR term through the split dense kernels."""
     import torch

@@ -39,8 +39,9 @@ def _with_workspace(wq, xd, D, nnz):
 
 # (M, N, K, nnz per 200 weights): a CSR product whose GEMM splits K with the sparse
 # term in the slice sum, then a smaller split one (64 x 256 tiles), then a dense
-# split one and a decode-sized one
-CASES = [(200, 256, 4096, 1), (40, 96, 2048, 1), (64, 520, 2048, 0), (4, 300, 1024, 1)]
+# split one, a decode-sized one, and a CSR product whose GEMM does not split K (one
+# fp32 slice, then the sum with the sparse term)
+CASES = [(200, 256, 4096, 1), (40, 96, 2048, 1), (64, 520, 2048, 0), (4, 300, 1024, 1), (300, 2048, 1024, 1)]
 
 
 def test_noalloc_matches_workspace_entry_point(gpu_lib):

@@ -81,6 +81,12 @@ CONFIGS = {
 }
 
 
+# Outlier density of the dense-and-sparse decomposition (0.45 % of the weights, the
+# batched-decode layer's) given to a layer whose configuration has none, to time and
+# check the prefill GEMM with a CSR term.
+SPARSE_PPM_DENSE_AND_SPARSE = 4500
+
+
 def _draw_weights(rng: np.random.Generator, cfg: Config, N: int, K: int) -> np.ndarray:
     W = rng.standard_normal((N, K), dtype=np.float32)
     W *= np.float32(cfg.sigma)
