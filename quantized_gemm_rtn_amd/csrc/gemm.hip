@@ -788,22 +788,25 @@ __device__ __forceinline__ void load_halves(const f16* p, float (&o)[VM]) {
 }
 
 // y = sum of the S fp32 K-slices + W_sparse x, for NC output channels per block and
-// all rows in chunks of 64 VM. Sparse term: wave w takes channels n0 + w and
-// n0 + w + 8; each lane holds VM rows and adds, for every CSR entry (c, v) of the
-// channel in order, v * xt[c][rows] (eight entries' loads in flight at once).
-// The per-(row, channel) sums pass through LDS to the fixed-order slice sum.
+// rows in chunks of 64 VM. Block b takes row chunks b % C, b % C + C, ... (C a
+// divisor of 8) of channel block b / C: blocks are dealt to the 8 XCDs in turn, so
+// every block on one XCD gathers from the same rows of xt, which then stay in that
+// XCD's L2. Sparse term: wave w takes channels n0 + w and n0 + w + 8; each lane
+// holds VM rows and adds, for every CSR entry (c, v) of the channel in order,
+// v * xt[c][rows] (eight entries' loads in flight at once). The per-(row, channel)
+// sums pass through LDS to the fixed-order slice sum.
 template <int VM>
 __global__ void __launch_bounds__(512)
 splitk_sparse_reduce_kernel(const float* __restrict__ ws, int S, int M, int N, const f16* __restrict__ xt, int Mp,
                             const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-                            const f16* __restrict__ val, void* __restrict__ y, int y_f32) {
+                            const f16* __restrict__ val, void* __restrict__ y, int y_f32, int C) {
   constexpr int NC = 16, MC = 64 * VM, NW = 8;
   __shared__ float sp[NC][MC + 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int n0 = blockIdx.x * NC;
+  const int n0 = (blockIdx.x / C) * NC;
   const size_t MN = (size_t)M * N;
-  for (int mb = 0; mb < M; mb += MC) {
+  for (int mb = (blockIdx.x % C) * MC; mb < M; mb += MC * C) {
     const int mrow = mb + VM * lane;
     const int mr = mrow < Mp ? mrow : 0;  // lanes past the padded rows read row 0
 #pragma unroll
@@ -1060,13 +1063,26 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
       e = sp_kernel ? launch_tile<128, 256, 1, 4, true>(a, stream) : launch_tile<128, 256, 1, 4, false>(a, stream);
     if (e != hipSuccess) return e;
     if (p.sparse_in_reduce) {
-      const int vm = mc > 256 ? 8 : mc > 128 ? 4 : mc > 64 ? 2 : 1;
-      const dim3 rgrid((unsigned)((N + 15) / 16));
+      // Up to 512 rows: one chunk per block (the gather's loads 2 VM bytes per lane).
+      // More rows: chunks of 256 dealt to the XCDs (C of them, C a divisor of 8) when
+      // such a chunk of xt (K x 256 halves) fits well inside one XCD's 4 MB L2, so
+      // that the gather reads it from there rather than from the memory-side cache
+      // (prefill layer with 0.45 % outliers: 378-383 against 407-410 us). Dealt at 64
+      // or 128 rows per chunk, the 70B layer at M = 512 lost 7-90 us (eight times the
+      // CSR walks, 2-byte loads), and its K = 28672 leaves no chunk inside one L2.
+      int vm = mc > 256 ? 8 : mc > 128 ? 4 : mc > 64 ? 2 : 1;
+      int C = 1;
+      if (mc > 512 && K * 256 * 2 <= ((int64_t)5 << 19)) {
+        vm = 4;
+        const int64_t chunks = (mc + 255) / 256;
+        C = chunks > 4 ? 8 : chunks > 2 ? 4 : 2;
+      }
+      const dim3 rgrid((unsigned)((N + 15) / 16 * C));
 #define WQ_SPRED(VM)                                                                                         \
   if (vm == VM)                                                                                              \
   hipLaunchKernelGGL(splitk_sparse_reduce_kernel<VM>, rgrid, dim3(512), 0, stream,                          \
                      static_cast<const float*>(workspace), p.ksplit, (int)mc, (int)N, xt, (int)Mp, row_ptr, col, \
-                     reinterpret_cast<const f16*>(val), yout, y_f32)
+                     reinterpret_cast<const f16*>(val), yout, y_f32, C)
       WQ_SPRED(1);
       WQ_SPRED(2);
       WQ_SPRED(4);
