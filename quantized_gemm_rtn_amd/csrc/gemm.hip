@@ -804,7 +804,16 @@ splitk_sparse_reduce_kernel(const float* __restrict__ ws, int S, int M, int N, c
   __shared__ float sp[NC][MC + 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int n0 = (blockIdx.x / C) * NC;
+  // channel block: in each group of 16 / C channel blocks, position p runs on the
+  // XCD of p mod (8 / C), so position p takes channel block 2 (p mod H) + p / H
+  // (H = 8 / C): channel blocks 2j and 2j + 1, the two 64-byte halves of a row's
+  // 128-byte lines of partial sums, are read through one L2 (blocks dealt to the
+  // XCDs in turn would otherwise put them on two). The last group of fewer keeps
+  // the plain order; with C == 8 the order is the plain one.
+  int nb = blockIdx.x / C;
+  const int nblk = gridDim.x / C, H = 8 / C, gs = 2 * H;
+  if ((nb / gs) * gs + gs <= nblk) nb = (nb / gs) * gs + 2 * (nb % H) + (nb % gs) / H;
+  const int n0 = nb * NC;
   const size_t MN = (size_t)M * N;
   for (int mb = (blockIdx.x % C) * MC; mb < M; mb += MC * C) {
     const int mrow = mb + VM * lane;
