@@ -378,6 +378,7 @@ gemm_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kBigSS = 128;                // halves per super-step (one group)
 constexpr int kXtPerThread = 2;            // transpose items per thread and super-step (XT)
+constexpr int64_t kBigFillBlocks = 256;     // one block per compute unit
 constexpr int kBigSzBytes = 2 * 2 * 256 * 4;  // (s, z) table: 2 buffers x 2 groups x 256 columns
 
 // Dense kernel for large M. As launched: block tile 128 x 256, four waves side by
@@ -413,7 +414,8 @@ gemm_big_kernel(GemmArgs a) {
   constexpr int XP = XV / 4;                  // ... per part
   constexpr int XR = T / 16;                  // rows between a thread's activation loads
   constexpr int STAGE = BM * kBigSS;          // rows of 256 bytes, 16-byte chunks swizzled
-  static_assert((T == 256 || T == 512) && BN == 256 && XP * 4 == XV && (NT == 2 || NT == 4) && MT >= NT,
+  static_assert((T == 256 || T == 512) && (BN == 256 || BN == 128) && XP * 4 == XV && (NT == 1 || NT == 2 || NT == 4) &&
+                    MT >= NT,
                 "tile/thread mismatch");
 
   extern __shared__ __align__(16) f16 smem[];
@@ -876,7 +878,7 @@ splitk_sparse_reduce_kernel(const float* __restrict__ ws, int S, int M, int N, c
 struct GemmPlan {
   int bm, bn;
   // 0: gemm_kernel; 1: gemm_big_kernel 128 x 256; 2 (M <= 64): gemm_big_kernel 64 x 256
-  // with weight windows of four or two super-steps
+  // or 64 x 128 (bn) with weight windows of four or two super-steps
   int kind;
   int ksplit, k_per_slice;
   // the sparse term is added in the slice sum (of one slice or several), from
@@ -895,16 +897,30 @@ static GemmPlan plan_gemm_kind(int64_t M, int64_t N, int64_t K, bool sparse) {
   p.kind = sparse ? 0 : (M > 128 && G % 2 == 0 ? 1 : (M <= 64 && G % 4 == 0 ? 2 : 0));
   p.bm = p.kind == 1 ? 128 : (M <= 64 ? 64 : 128);
   p.bn = 256;
-  const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+  int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   int64_t s = 1;
   if (p.kind != 0) {
     // split K while the grid is below two blocks per CU (large M) or one (M <= 64,
     // where longer slices amortize each block's first loads and partial stores better
     // than a second block per CU hides latency), and each slice keeps >= 8 groups;
     // slices are a multiple of two (large M) or four (M <= 64) groups
-    const int64_t target = p.kind == 2 ? 256 : 512;
     const int64_t groups = K / 128;
-    while (tiles * s * 2 <= target && groups / (s * 2) >= 8) s *= 2;
+    const auto split = [&](int64_t tl, int64_t target) {
+      int64_t sp = 1;
+      while (tl * sp * 2 <= target && groups / (sp * 2) >= 8) sp *= 2;
+      return sp;
+    };
+    s = split(tiles, p.kind == 2 ? 256 : 512);
+    // M <= 64 on a layer whose 64 x 256 tiles and slices leave CUs without a block:
+    // 64 x 128 tiles instead (each wave one 32-column subtile), up to two blocks per
+    // CU. Measured with the GEMM forced: 4096 x 4096 at M = 32 and 64 19.4 and 20.4
+    // against 24.8 and 25.0 us. On the 70B down-projection, whose 256-wide grid has a
+    // block on every CU, 128-wide tiles took 76.9 against 70.5 us at M = 64.
+    if (p.kind == 2 && tiles * s < kBigFillBlocks) {
+      p.bn = 128;
+      tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+      s = split(tiles, 2 * kBigFillBlocks);
+    }
     p.ksplit = (int)s;
     const int64_t q = p.kind == 1 ? 2 : 4;  // slices: a multiple of q groups
     const int64_t per = ((groups + s - 1) / s + q - 1) / q * q;
@@ -943,11 +959,16 @@ static GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool sparse) {
   return plan_gemm_kind(M, N, K, sparse);
 }
 
-// blocks of the dense product's GEMM launch for this shape (given a full workspace)
-int64_t gemm_grid_blocks(int64_t M, int64_t N, int64_t K) {
+// the dense product's GEMM plan for this shape (given a full workspace)
+GemmPlanInfo gemm_plan_info(int64_t M, int64_t N, int64_t K) {
   const GemmPlan p = plan_gemm(M, N, K, false);
   const int64_t bm = p.kind == 1 ? 128 : p.bm;
-  return ((M + bm - 1) / bm) * ((N + p.bn - 1) / p.bn) * p.ksplit;
+  GemmPlanInfo i;
+  i.blocks = ((M + bm - 1) / bm) * ((N + p.bn - 1) / p.bn) * p.ksplit;
+  i.ksplit = p.ksplit;
+  i.big = p.kind != 0;
+  i.bn = p.bn;
+  return i;
 }
 
 // enough for the dense and the sparse plan of the shape, and for the tile kernel's
@@ -1031,7 +1052,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
                   ? reinterpret_cast<f16*>(static_cast<char*>(workspace) + partials_bytes(p, mc, N))
                   : nullptr;
     // the GEMM writes x^T itself when its blocks' shares fit (wide layers); else a launch
-    const int64_t big_bm = p.kind == 1 ? 128 : 64, tn = (N + 255) / 256;
+    const int64_t big_bm = p.kind == 1 ? 128 : 64, tn = (N + p.bn - 1) / p.bn;
     const bool xt_in_gemm = p.sparse_in_reduce && (kBigSS + tn - 1) / tn * big_bm <= kXtPerThread * 256 &&
                             (size_t)K * (size_t)Mp * 2 < ((size_t)1 << 31);
     if (p.sparse_in_reduce && !xt_in_gemm) {
@@ -1072,9 +1093,9 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
     if (p.kind == 1)
       e = launch_big<128, 256, 1, 4, 2, 1>(a, stream);
     else if (p.kind == 2 && per % 8 == 0 && G % 8 == 0)
-      e = launch_big<64, 256, 1, 4, 2, 4>(a, stream);
+      e = p.bn == 128 ? launch_big<64, 128, 1, 4, 2, 4>(a, stream) : launch_big<64, 256, 1, 4, 2, 4>(a, stream);
     else if (p.kind == 2)
-      e = launch_big<64, 256, 1, 4, 2, 2>(a, stream);
+      e = p.bn == 128 ? launch_big<64, 128, 1, 4, 2, 2>(a, stream) : launch_big<64, 256, 1, 4, 2, 2>(a, stream);
     else if (!f.plain())
       e = launch_tile_fmt(a, p.bm, sp_kernel, f, stream);
     else if (p.bm == 64)

@@ -207,15 +207,27 @@ size_t wq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return wq::gemm_workspace_bytes(M, N, K);
 }
 
-// The decode kernels re-read the weights once per 16 rows, the GEMM reads them once
-// but needs a grid that fills the GPU. Measured on the 4096 x 4096 layer with its
-// CSR (the GEMM splits K at most twice there: 32 blocks), the decode kernel stays
-// faster up to M = 64 (25.8 against 28.1 us); on the 8192 x 28672 layer (256
-// blocks) the GEMM takes over from M = 20 (64.1 against 77.3 us).
+// The decode kernels re-read the weights once per 16 rows (their time steps up at
+// M = 17, 33 and 49), the GEMM reads them once but needs a grid that fills the GPU.
+// Measured (decode kernel / GEMM, us, both forced):
+//  - 8192 x 28672 (64 x 256 tiles, a block on every CU): the GEMM from M = 20
+//    (77.3 / 64.1; at M = 16 49.7 / 63.4);
+//  - 4096 x 4096 with its CSR and 11008 x 4096 (64 x 128 tiles, four K slices):
+//    the decode kernel to M = 32 (15.6 / 19.4, 18.9 / 22.1), the GEMM from M = 40
+//    (20.3 / 19.9, 27.9 / 22.6);
+//  - 8192 x 3584 (28 groups, two K slices): the decode kernel to M = 48
+//    (22.3 / 23.6), the GEMM at M = 64 (27.8 / 24.6).
+// Shapes that take the tile GEMM (a group count that is not a multiple of four)
+// keep the rule measured before these tiles: the decode kernel while the GEMM's
+// grid has fewer than 128 blocks.
 int wq_auto_kernel(int64_t M, int64_t N, int64_t K) {
   if (M <= 16) return WQ_KERNEL_GEMV;
-  if (M <= 64 && N >= 1 && K >= kGroup && K % kGroup == 0 && wq::gemm_grid_blocks(M, N, K) < 128)
-    return WQ_KERNEL_GEMV;
+  if (M > 64 || N < 1 || K < kGroup || K % kGroup != 0) return WQ_KERNEL_GEMM;
+  const wq::GemmPlanInfo p = wq::gemm_plan_info(M, N, K);
+  if (!p.big) return p.blocks < 128 ? WQ_KERNEL_GEMV : WQ_KERNEL_GEMM;
+  if (p.bn == 256) return WQ_KERNEL_GEMM;
+  if (M <= 32) return WQ_KERNEL_GEMV;
+  if (M <= 48 && p.ksplit < 4) return WQ_KERNEL_GEMV;
   return WQ_KERNEL_GEMM;
 }
 

@@ -95,8 +95,16 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // ... of the plan one product takes (4-bit codes, 128-channel groups; a CSR term or
 // not); at most gemm_workspace_bytes(M, N, K)
 size_t gemm_plan_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sparse);
-// blocks of the dense GEMM's launch for M x N x K (split K included)
-int64_t gemm_grid_blocks(int64_t M, int64_t N, int64_t K);
+// the dense GEMM's plan for M x N x K: blocks of its launch (split K included), K
+// slices, whether it is gemm_big_kernel, and its tile width (256, or 128 for M <= 64
+// where 256-wide tiles would leave compute units without a block)
+struct GemmPlanInfo {
+  int64_t blocks;
+  int ksplit;
+  bool big;
+  int bn;
+};
+GemmPlanInfo gemm_plan_info(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, int64_t K, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                        const int32_t* col, const uint16_t* val, int64_t nnz, void* y, int y_f32, void* workspace,

@@ -55,15 +55,25 @@ def test_status_strings(lib):
 
 
 def test_auto_kernel(lib):
+    """The measured crossover: the decode kernel (1) up to M = 16 everywhere; from
+    M = 17 the GEMM (2) on the 70B layer, whose 64 x 256 tiles give every CU a block;
+    on smaller layers (64 x 128 tiles) the decode kernel to M = 32, then to M = 48
+    where the GEMM splits K fewer than four ways (28 groups), the GEMM above; the
+    decode kernel while the tile GEMM's grid has under 128 blocks (group counts that
+    are not a multiple of four)."""
     assert lib.wq_auto_kernel(1, 11008, 4096) == 1
     assert lib.wq_auto_kernel(16, 4096, 4096) == 1
-    # measured crossover: the 4096 x 4096 layer keeps the decode kernel up to M = 64
-    # (its GEMM grid is 32 blocks), the 70B down-projection switches at M = 17
-    assert lib.wq_auto_kernel(17, 4096, 4096) == 1
-    assert lib.wq_auto_kernel(64, 4096, 4096) == 1
-    assert lib.wq_auto_kernel(65, 4096, 4096) == 2
+    assert lib.wq_auto_kernel(16, 8192, 28672) == 1
     assert lib.wq_auto_kernel(17, 8192, 28672) == 2
     assert lib.wq_auto_kernel(64, 8192, 28672) == 2
+    for N, K in [(4096, 4096), (11008, 4096)]:
+        assert lib.wq_auto_kernel(32, N, K) == 1
+        assert lib.wq_auto_kernel(33, N, K) == 2
+        assert lib.wq_auto_kernel(64, N, K) == 2
+    assert lib.wq_auto_kernel(48, 8192, 3584) == 1
+    assert lib.wq_auto_kernel(49, 8192, 3584) == 2
+    assert lib.wq_auto_kernel(40, 300, 3 * 128) == 1      # tile GEMM, 2 blocks
+    assert lib.wq_auto_kernel(65, 4096, 4096) == 2
     assert lib.wq_auto_kernel(2048, 14336, 4096) == 2
 
 
