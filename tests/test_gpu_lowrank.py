@@ -59,7 +59,7 @@ def test_lowrank_parity(gpu_lib, M, N, K, r, sparse, kernel):
 
 
 @pytest.mark.parametrize("kernel", ["gemv", "gemm"])
-@pytest.mark.parametrize("M,K", [(1, 1024), (16, 2048), (40, 1024), (200, 4096), (300, 1024)])
+@pytest.mark.parametrize("M,K", [(1, 1024), (2, 4096), (16, 2048), (40, 1024), (200, 4096), (300, 1024)])
 def test_lowrank_integer_exact_fp32(gpu_lib, kernel, M, K):
     """Integer codes, zero-points, activations, sparse values and factors with
     power-of-two scales: t = x . L1^T holds integers up to 1024 (exact in fp16)
@@ -127,3 +127,35 @@ def test_lowrank_integer_exact_tall_batch(gpu_lib):
     y = _run(gpu_lib, torch, L, D, x, L1, L2, "auto", True, out_dtype=torch.float32)
     ref = oracle.linear_ref(x, q, s, z, rp, col, val, L1=L1, L2=L2)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("M,N,K,r,sparse,kernel", [
+    (1, 300, 1024, 32, True, "gemv"),      # block-staged decode kernel
+    (2, 130, 2048, 64, False, "gemv"),
+    (1, 200, 12288, 32, True, "gemv"),     # long row (the single-row kernel takes no branch): block-staged
+    (5, 300, 1536, 96, True, "gemv"),      # per-wave staging kernel
+    (9, 1100, 3584, 256, False, "gemv"),   # rank 256, 28 groups
+    (100, 300, 1152, 64, True, "auto"),    # tile GEMM
+])
+def test_lowrank_consecutive_calls(gpu_lib, M, N, K, r, sparse, kernel):
+    """Five calls in a row on the same layer and workspace with new activations
+    each time, every one against the oracle: a t left in the workspace by the
+    previous call would fail."""
+    import torch
+    W = workloads.random_weights(7 * M + N + r, N, K)
+    L = oracle.quantize_layer(W, N * K // 250 if sparse else 0)
+    L1, L2 = workloads.lowrank_factors(M + 5 * r, r, N, K)
+    D = layer_to_dev(L, torch)
+    L1d, L2d = to_dev(L1, torch), to_dev(L2, torch)
+    ws = torch.empty(max(gpu_lib.linear_lowrank_workspace_bytes(M, N, K, r), 1), dtype=torch.uint8, device="cuda")
+    args = (L["row_ptr"], L["col"], L["val"]) if sparse else (None, None, None)
+    dargs = (D["row_ptr"], D["col"], D["val"]) if sparse else (None, None, None)
+    say(f"[lowrank consecutive] M={M} N={N} K={K} r={r} sparse={sparse} kernel={kernel}")
+    for call in range(5):
+        x = workloads.random_x(1000 + 17 * call + M, M, K)
+        y = gpu_lib.linear_lowrank(to_dev(x, torch), D["packed"], D["scales"], D["zeros"], L1d, L2d, *dargs,
+                                   kernel=kernel, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.linear_ref(x, L["q"], L["s"], L["z"], *args, L1=L1, L2=L2)
+        err = oracle.rel_err_inf(y.float().cpu().numpy(), ref)
+        assert err <= TOL, (call, err)
