@@ -53,10 +53,17 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
                  : G <= kSzMaxG<1>                             ? 1
                                                                : 0;
   const bool vec = sv == 8;
-  // scales and zero-points in registers, two loads per window of D groups: every
-  // wave's window starts on a multiple of D groups
+  // scales and zero-points in registers, two loads per window of D groups, when each
+  // wave has exactly one window (4096 input channels): there they skip the block's
+  // LDS staging (headline layer 6.43 against 6.85 us). With more windows each one
+  // reloads them inside the weight stream, and staging the block's (s, z) once with
+  // the activations is faster for one row (70B down-projection with the MFMA kernel
+  // 28.6 against 30.5 us, with a rank-32 branch 31.8 against 33.6; K = 8192 11.3
+  // against 11.6) and for two rows at K = 8192 (13.5 against 14.1 us), but not for two
+  // rows from K = 12288 on (22.8 against 22.2 us, K = 16384 28.6 against 28.0).
   static_assert(kGemvDepth == 4 || kGemvDepth == 8, "in-register (s, z) windows hold 4 or 8 groups");
-  const bool in_regs = vec && G % (kGemvDepth * kGemvWaves) == 0;
+  const bool in_regs = vec && G % (kGemvDepth * kGemvWaves) == 0 &&
+                       (G == kGemvDepth * kGemvWaves || (mrows_max == 2 && G >= 96));
   const int sz_mode = in_regs ? kSzInRegs : sv;
   // output rows a lane can hold: rows 4h .. 4h+3 of the tile, so M = 1, 2 need fewer
   const int mr = mrows_max == 1 ? 1 : (mrows_max == 2 ? 2 : 4);
