@@ -23,7 +23,8 @@ static hipError_t launch_ring(const uint16_t* x, int64_t M, int64_t K, const uin
                               const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                               const int32_t* col, const uint16_t* val, void* y, int y_f32, const LowRank& lr,
                               hipStream_t stream) {
-  const size_t lds = (size_t)NT * 16 * (K / kGroup + 1) * 4 + (size_t)kGemvWaves * 4 * XL * 136 * 2;
+  const size_t lds = (SZV == kSzInRegs ? 0 : (size_t)NT * 16 * (K / kGroup + 1) * 4) +
+                     (size_t)kGemvWaves * 4 * XL * 136 * 2;
   return launch_rows(gemv_ring_kernel<kGemvWaves, kGemvRingDepth, XL, NT, SZV, SP>, lds, 16 * NT, x, M, K, packed,
                      scales, zeros, N, row_ptr, col, val, y, y_f32, lr, stream);
 }
@@ -95,7 +96,15 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   // CUs, 1.49x, run faster as 688 single tiles)
   const int64_t pairs = ((N + 31) / 32) * ((M + 15) / 16);
   const int nt = pairs >= kNumCu && (pairs + kNumCu - 1) / kNumCu * kNumCu * 100 <= 115 * pairs ? 2 : 1;
+  // per-wave staging with (s, z) in registers, loaded per window of D groups with its
+  // weights, when each wave has at most two windows (up to 4096 input channels):
+  // 4096 x 4096 at M = 16, 8 and 4 9.7, 7.3 and 6.7 against 10.2, 7.6 and 7.1 us,
+  // the 11008 x 4096 layer at M = 16 13.4 against 13.5. On the 70B down-projection
+  // (14 windows per wave) the reloads inside the weight stream cost more than the
+  // block's staging saves: 43.3 against 38.4 us at M = 8.
+  const bool ring_regs = vec && G % (kGemvRingDepth * kGemvWaves) == 0 && G <= 2 * kGemvRingDepth * kGemvWaves;
 #define WQ_RING_SV(XL, NT, SP)                                   \
+  if (ring_regs) return launch_ring<XL, NT, kSzInRegs, SP>(WQ_ARGS); \
   if (sv == 8) return launch_ring<XL, NT, 8, SP>(WQ_ARGS);       \
   if (sv == 4) return launch_ring<XL, NT, 4, SP>(WQ_ARGS);       \
   if (sv == 2) return launch_ring<XL, NT, 2, SP>(WQ_ARGS);       \

@@ -636,6 +636,9 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
 // Rows of the slot are 272 bytes apart, so the 16 rows of a fragment read fall in
 // distinct banks. One wave writes and reads its slot, and LDS instructions of a
 // wave execute in order, so no barrier is involved.
+// SZV == kSzInRegs (4-bit codes, 128-channel groups, windows starting at multiples
+// of D): each lane loads the (s, z) of its rows for a window of D groups as two
+// vectors, issued with the window's weights, and the block stages nothing.
 template <int KW, int D, int XL, int NT, int SZV, bool SP, int BITS = 4, bool G64 = false>
 __global__ void __launch_bounds__(64 * KW)
 gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
@@ -645,6 +648,8 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
                  const f16* __restrict__ lr_up, int lr_r) {
   constexpr int T = 64 * KW;
   static_assert(T <= kGemvMaxThreads, "MFMA results of larger blocks were clobbered (see hold_accumulator)");
+  constexpr bool kRegs = SZV == kSzInRegs;
+  static_assert(!kRegs || (BITS == 4 && !G64 && (D == 4 || D == 8)), "in-register (s, z): 4-bit, 4 or 8 groups");
   constexpr int R = 4 * XL;          // rows staged per group
   constexpr int kRowHalves = 136;    // 128 + 8
   extern __shared__ __align__(16) char smem[];
@@ -656,8 +661,8 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
   const int G = K >> 7;
   const int Gs = G64 ? 2 * G : G;  // (s, z) per row: one per 64 or per 128 input channels
   const int mrows = min(16, M - m0);
-  f16x2* sz = reinterpret_cast<f16x2*>(smem);  // NT x [16][Gs + 1]: (s, 1024 + z)
-  f16* slot = reinterpret_cast<f16*>(smem + (size_t)NT * 16 * (Gs + 1) * 4) + wave * (R * kRowHalves);
+  f16x2* sz = reinterpret_cast<f16x2*>(smem);  // NT x [16][Gs + 1]: (s, 1024 + z), unless kRegs
+  f16* slot = reinterpret_cast<f16*>(smem + (kRegs ? 0 : (size_t)NT * 16 * (Gs + 1) * 4)) + wave * (R * kRowHalves);
 
   using WT = typename WRun<BITS>::type;
   constexpr int GW = WRun<BITS>::group_words;
@@ -685,9 +690,23 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
       sp_e1[j] = row_ptr[nr + 1];
     }
   }
-  SzStage<SZV, T> szs[NT];
+  SzStage<kRegs ? 8 : SZV, T> szs[NT];
+  using SzVec = typename SzVecOf<(D == 4 || D == 8) ? D : 8>::type;
+  const f16* s_row[NT];
+  const f16* z_row[NT];
+  SzVec sv[NT], zv[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) szs[j].load(scales, zeros, min(n0 + 16 * j, N - 1), N, Gs, t);
+  for (int j = 0; j < NT; ++j) {
+    if constexpr (kRegs) {
+      const size_t o = (size_t)min(n0 + 16 * j + r, N - 1) * G + g_lo;
+      s_row[j] = scales + o;
+      z_row[j] = zeros + o;
+      sv[j] = *reinterpret_cast<const SzVec*>(s_row[j]);
+      zv[j] = *reinterpret_cast<const SzVec*>(z_row[j]);
+    } else {
+      szs[j].load(scales, zeros, min(n0 + 16 * j, N - 1), N, Gs, t);
+    }
+  }
   const int g_first_valid = min(g_lo, G - 1);
   WT wbuf[D][NT];
   uint4 xbuf[D][XL];
@@ -699,10 +718,12 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
 #pragma unroll
     for (int j = 0; j < XL; ++j) xbuf[i][j] = *reinterpret_cast<const uint4*>(xst[j] + (size_t)g * 128);
   }
+  if constexpr (!kRegs) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
-    szs[j].store(sz + j * 16 * (Gs + 1), scales, zeros, min(n0 + 16 * j, N - 1), N, Gs, t);
-  __syncthreads();
+    for (int j = 0; j < NT; ++j)
+      szs[j].store(sz + j * 16 * (Gs + 1), scales, zeros, min(n0 + 16 * j, N - 1), N, Gs, t);
+    __syncthreads();
+  }
   // the first CSR entries of each row, behind the initial weight prefetch
   constexpr int HB = kSparseBatch / NT;
   SparseHead<HB, KW> sph[NT];
@@ -719,7 +740,9 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto group = [&](const WT* w, const uint4* xg, int g) {
+  const f16 k1024 = (f16)1024.0f;
+  // group g, position i of its window
+  auto group = [&](const WT* w, const uint4* xg, int g, int i) {
 #pragma unroll
     for (int j = 0; j < XL; ++j) *reinterpret_cast<uint4*>(slot + (h + 4 * j) * kRowHalves + 8 * r) = perm_x8(xg[j]);
     uint4 xa[4];
@@ -729,7 +752,12 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
     for (int j = 0; j < NT; ++j) {
       // with 64-channel groups, lanes h = 0, 1 and h = 2, 3 fall in different groups,
       // so the scale goes into the operand; otherwise it scales the group's sum
-      const f16x2 sbz = szr[j * 16 * (Gs + 1) + (G64 ? 2 * g + (h >> 1) : g)];
+      f16x2 sbz;
+      if constexpr (kRegs) {
+        sbz = f16x2{half_of(sv[j], i), (f16)(k1024 + half_of(zv[j], i))};
+      } else {
+        sbz = szr[j * 16 * (Gs + 1) + (G64 ? 2 * g + (h >> 1) : g)];
+      }
       const f16x2 bias = {sbz[1], sbz[1]};
       const f16 nb = (f16)960.0f - sbz[1];  // -(64 + z)
       const f16x2 nbias16 = {nb, nb};
@@ -750,16 +778,37 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
   int gs = 0;
   for (int b = 0; b + 1 < win.n; ++b) {
     const int gs_next = win.next(b, gs);
+    SzVec sn[NT], zn[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      sn[j] = sv[j];
+      zn[j] = zv[j];
+    }
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      group(wbuf[i], xbuf[i], g_lo + gs + i);
+      group(wbuf[i], xbuf[i], g_lo + gs + i, i);
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         wbuf[i][j] = *reinterpret_cast<const WT*>(wrow[j] + (size_t)(g_lo + gs_next + i) * GW);
 #pragma unroll
       for (int j = 0; j < XL; ++j)
         xbuf[i][j] = *reinterpret_cast<const uint4*>(xst[j] + (size_t)(g_lo + gs_next + i) * 128);
+      // in-register mode: the next window's (s, z) right after its first weights
+      if constexpr (kRegs) {
+        if (i == 0) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            sn[j] = *reinterpret_cast<const SzVec*>(s_row[j] + gs_next);
+            zn[j] = *reinterpret_cast<const SzVec*>(z_row[j] + gs_next);
+          }
+        }
+      }
       __builtin_amdgcn_sched_barrier(kSchedKeepGroups);  // keep the refill next to its consumption
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      sv[j] = sn[j];
+      zv[j] = zn[j];
     }
     gs = gs_next;
   }
@@ -776,11 +825,11 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
   }
   if (win.last_lo == 0 && win.last_hi == D) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) group(wbuf[i], xbuf[i], g_lo + gs + i);
+    for (int i = 0; i < D; ++i) group(wbuf[i], xbuf[i], g_lo + gs + i, i);
   } else {
 #pragma unroll
     for (int i = 0; i < D; ++i)
-      if (i >= win.last_lo && i < win.last_hi) group(wbuf[i], xbuf[i], g_lo + gs + i);
+      if (i >= win.last_lo && i < win.last_hi) group(wbuf[i], xbuf[i], g_lo + gs + i, i);
   }
 
   if constexpr (SP) {
