@@ -16,12 +16,15 @@
 //    512-channel steps, accumulate x . L1[j] with fp16 dot2 into fp32 per row, sum
 //    their lanes by recursive halving (each exchange hands half of a lane's rows to
 //    its partner) and their waves through LDS in wave order, and store fp16 t.
-//  lowrank_down_kernel (more rows): one block per 16 rows of x, 32 components of
-//    the rank and chunk of at most 128 steps of 32 input channels (the chunks are
-//    sized so that the grid has about a block per CU); each of its sixteen waves
-//    takes every sixteenth step of the chunk, with all its loads issued up front,
-//    and feeds two 16x16x32 fp16 MFMAs per step (x rows in A, rows of L1 in B, fp32
-//    accumulation), so each row of x is read once per 32 components. The waves'
+//  lowrank_down_kernel (more rows): one block per 16 rows of x, CT = 32 (or 16)
+//    components of the rank and chunk of at most 128 steps of 32 input channels
+//    (the chunks are sized so that the grid has about a block per CU); each of its
+//    sixteen waves takes every sixteenth step of the chunk, with all its loads
+//    issued up front, and feeds CT / 16 16x16x32 fp16 MFMAs per step (x rows in A,
+//    rows of L1 in B, fp32 accumulation), so each row of x is read once per CT
+//    components. Blocks of 16 components are used where K fits one chunk and the
+//    32-component tiles give at least half of the CUs but not all of them a block:
+//    twice the blocks, each with two thirds of the loads, and still no partials. The waves'
 //    tiles are summed through LDS in a fixed order; with a single chunk the block
 //    rounds the sum to fp16 t itself, else it stores the chunk's fp32 partial and
 //  lowrank_finish_kernel: t = fp16 of the sum of the chunks' partials in chunk
@@ -43,10 +46,12 @@ constexpr int64_t kLrTargetBlocks = 256;  // about one block per CU
 // chunk; otherwise enough chunks for about a block per CU, but at least one step
 // for each of a block's waves.
 struct LrPlan {
-  int steps, chunks;
+  int steps, chunks, ct;  // ct: components per block (32 or 16)
 };
 static LrPlan lowrank_plan(int64_t M, int64_t K, int64_t r) {
-  const int64_t nsteps = K / 32, tiles = ((M + 15) / 16) * (r / 32);
+  const int64_t nsteps = K / 32, tiles32 = ((M + 15) / 16) * (r / 32);
+  const int ct = nsteps <= kLrChunkSteps && tiles32 >= kLrTargetBlocks / 2 && tiles32 < kLrTargetBlocks ? 16 : 32;
+  const int64_t tiles = ct == 16 ? 2 * tiles32 : tiles32;
   int64_t chunks = (nsteps + kLrChunkSteps - 1) / kLrChunkSteps;
   if (!(chunks == 1 && tiles >= kLrTargetBlocks / 2)) {
     const int64_t want = (kLrTargetBlocks + tiles - 1) / tiles;
@@ -55,7 +60,7 @@ static LrPlan lowrank_plan(int64_t M, int64_t K, int64_t r) {
     chunks = chunks < cap ? chunks : cap;
   }
   const int64_t steps = (nsteps + chunks - 1) / chunks;
-  return LrPlan{(int)steps, (int)((nsteps + steps - 1) / steps)};
+  return LrPlan{(int)steps, (int)((nsteps + steps - 1) / steps), ct};
 }
 
 constexpr int64_t kLrRowsPerLaunch = 65535 * 16;  // gridDim.y limit
@@ -73,55 +78,58 @@ size_t lowrank_partial_bytes(int64_t M, int64_t K, int64_t r) {
   return most;
 }
 
+template <int CT>
 __global__ void __launch_bounds__(64 * kLrWaves)
 lowrank_down_kernel(const f16* __restrict__ x, int M, int K, const f16* __restrict__ L1, int r, int cs,
                     float* __restrict__ part, f16* __restrict__ t) {
+  static_assert(CT == 16 || CT == 32, "16 or 32 components per block");
+  constexpr int U = CT / 16;  // 16x16 tiles per block
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane & 15, h = lane >> 4;
-  const int j0 = blockIdx.x * 32, m0 = blockIdx.y * 16, chunk = blockIdx.z;
+  const int j0 = blockIdx.x * CT, m0 = blockIdx.y * 16, chunk = blockIdx.z;
   const int s0 = chunk * cs, s1 = min(K / 32, s0 + cs);  // cs <= kLrChunkSteps
   // lane (h, q): row m0 + q of x (rows past M read row M - 1, never stored) and
-  // components j0 + q, j0 + 16 + q of L1 (r is a multiple of 32), channels
+  // components j0 + 16 u + q of L1 (r is a multiple of 32), channels
   // 32 s + 8 h .. + 7
   const f16* xr = x + (size_t)min(m0 + q, M - 1) * K + 8 * h;
   const f16* lr0 = L1 + (size_t)(j0 + q) * K + 8 * h;
-  const f16* lr1 = lr0 + (size_t)16 * K;
   // a wave's steps: s0 + wave + 16 i below s1 (a wave-uniform test: steps past the
   // chunk load nothing, where clamped reloads of one address would contend)
-  uint4 av[kLrStepsPerWave], bv[kLrStepsPerWave][2];
+  uint4 av[kLrStepsPerWave], bv[kLrStepsPerWave][U];
 #pragma unroll
   for (int i = 0; i < kLrStepsPerWave; ++i) {
     const int s = s0 + wave + kLrWaves * i;
     if (s < s1) {
       av[i] = *reinterpret_cast<const uint4*>(xr + 32 * s);
-      bv[i][0] = *reinterpret_cast<const uint4*>(lr0 + 32 * s);
-      bv[i][1] = *reinterpret_cast<const uint4*>(lr1 + 32 * s);
+#pragma unroll
+      for (int u = 0; u < U; ++u) bv[i][u] = *reinterpret_cast<const uint4*>(lr0 + (size_t)16 * u * K + 32 * s);
     }
   }
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kLrStepsPerWave; ++i)
     if (s0 + wave + kLrWaves * i < s1) {  // wave-uniform
-      acc[0] = mfma_16x16x32(as_f16x8(av[i]), as_f16x8(bv[i][0]), acc[0]);
-      acc[1] = mfma_16x16x32(as_f16x8(av[i]), as_f16x8(bv[i][1]), acc[1]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = mfma_16x16x32(as_f16x8(av[i]), as_f16x8(bv[i][u]), acc[u]);
     }
-  __shared__ f32x4 red[kLrWaves - 1][2][64];
+  __shared__ f32x4 red[kLrWaves - 1][U][64];
   if (wave > 0) {
-    red[wave - 1][0][lane] = acc[0];
-    red[wave - 1][1][lane] = acc[1];
+#pragma unroll
+    for (int u = 0; u < U; ++u) red[wave - 1][u][lane] = acc[u];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < kLrWaves - 1; ++w) {
-    acc[0] += red[w][0][lane];
-    acc[1] += red[w][1][lane];
-  }
+  for (int w = 0; w < kLrWaves - 1; ++w)
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] += red[w][u][lane];
   // D[4 h + i][q] of tile u: row m0 + 4 h + i, component j0 + 16 u + q
   const bool single = gridDim.z == 1;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + 4 * h + i;
@@ -255,10 +263,15 @@ hipError_t launch_lowrank_down(const uint16_t* x, int64_t M, int64_t K, const ui
     const LrPlan p = lowrank_plan(mc, K, r);
     const int chunks = p.chunks;
     f16* tm = reinterpret_cast<f16*>(t) + m * r;
-    const dim3 grid((unsigned)(r / 32), (unsigned)((mc + 15) / 16), (unsigned)chunks);
-    hipLaunchKernelGGL(lowrank_down_kernel, grid, dim3(64 * kLrWaves), 0, stream,
-                       reinterpret_cast<const f16*>(x) + m * K, (int)mc, (int)K, reinterpret_cast<const f16*>(L1),
-                       (int)r, p.steps, part, tm);
+    const dim3 grid((unsigned)(r / p.ct), (unsigned)((mc + 15) / 16), (unsigned)chunks);
+    if (p.ct == 16)
+      hipLaunchKernelGGL(lowrank_down_kernel<16>, grid, dim3(64 * kLrWaves), 0, stream,
+                         reinterpret_cast<const f16*>(x) + m * K, (int)mc, (int)K, reinterpret_cast<const f16*>(L1),
+                         (int)r, p.steps, part, tm);
+    else
+      hipLaunchKernelGGL(lowrank_down_kernel<32>, grid, dim3(64 * kLrWaves), 0, stream,
+                         reinterpret_cast<const f16*>(x) + m * K, (int)mc, (int)K, reinterpret_cast<const f16*>(L1),
+                         (int)r, p.steps, part, tm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (chunks > 1) {
