@@ -37,7 +37,7 @@ static hipError_t launch_ring_fmt(const uint16_t* x, int64_t M, int64_t K, const
                                   const uint16_t* scales, const uint16_t* zeros, int64_t N, const int32_t* row_ptr,
                                   const int32_t* col, const uint16_t* val, void* y, int y_f32, hipStream_t stream) {
   const int64_t Gs = (G64 ? 2 : 1) * (K / kGroup);
-  const size_t lds = (size_t)NT * 16 * (Gs + 1) * 4 + (size_t)kGemvWaves * 4 * XL * 136 * 2;
+  const size_t lds = (SZV == kSzInRegs ? 0 : (size_t)NT * 16 * (Gs + 1) * 4) + (size_t)kGemvWaves * 4 * XL * 136 * 2;
   return launch_rows(gemv_ring_kernel<kGemvWaves, kGemvRingDepth, XL, NT, SZV, SP, BITS, G64>, lds, 16 * NT, x, M, K,
                      packed, scales, zeros, N, row_ptr, col, val, y, y_f32, LowRank{}, stream);
 }
@@ -87,6 +87,17 @@ hipError_t launch_gemv_fmt(const uint16_t* x, int64_t M, int64_t K, const uint32
   const int xl = mrows_max <= 4 ? 1 : (mrows_max <= 8 ? 2 : 4);
   const int64_t pairs = ((N + 31) / 32) * ((M + 15) / 16);
   const int nt = pairs >= kNumCu && (pairs + kNumCu - 1) / kNumCu * kNumCu * 100 <= 115 * pairs ? 2 : 1;
+  // 3-bit codes with 128-channel groups: (s, z) in registers where each wave has at
+  // most two windows, as for 4-bit codes
+  const bool ring_regs = f.bits == 3 && !f.g64 && sv == 8 && G % (kGemvRingDepth * kGemvWaves) == 0 &&
+                         G <= 2 * kGemvRingDepth * kGemvWaves;
+#define WQ_RR(XL, NT)                                                              \
+  if (ring_regs && xl == XL && nt == NT) {                                         \
+    if (sp) return launch_ring_fmt<XL, NT, kSzInRegs, true, 3, false>(WQ_ARGS);    \
+    return launch_ring_fmt<XL, NT, kSzInRegs, false, 3, false>(WQ_ARGS);           \
+  }
+  WQ_RR(1, 1) WQ_RR(2, 1) WQ_RR(4, 1) WQ_RR(1, 2) WQ_RR(2, 2) WQ_RR(4, 2)
+#undef WQ_RR
 #define WQ_RF(XL, NT, SZ, B, G6)                                          \
   if (xl == XL && nt == NT && sv == SZ && f.bits == B && f.g64 == G6) {    \
     if (sp) return launch_ring_fmt<XL, NT, SZ, true, B, G6>(WQ_ARGS);     \

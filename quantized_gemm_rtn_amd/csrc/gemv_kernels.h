@@ -636,9 +636,9 @@ gemv_lds_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restr
 // Rows of the slot are 272 bytes apart, so the 16 rows of a fragment read fall in
 // distinct banks. One wave writes and reads its slot, and LDS instructions of a
 // wave execute in order, so no barrier is involved.
-// SZV == kSzInRegs (4-bit codes, 128-channel groups, windows starting at multiples
-// of D): each lane loads the (s, z) of its rows for a window of D groups as two
-// vectors, issued with the window's weights, and the block stages nothing.
+// SZV == kSzInRegs (128-channel groups, windows starting at multiples of D): each
+// lane loads the (s, z) of its rows for a window of D groups as two vectors,
+// issued with the window's weights, and the block stages nothing.
 template <int KW, int D, int XL, int NT, int SZV, bool SP, int BITS = 4, bool G64 = false>
 __global__ void __launch_bounds__(64 * KW)
 gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __restrict__ packed,
@@ -649,7 +649,7 @@ gemv_ring_kernel(const f16* __restrict__ x, int M, int K, const uint32_t* __rest
   constexpr int T = 64 * KW;
   static_assert(T <= kGemvMaxThreads, "MFMA results of larger blocks were clobbered (see hold_accumulator)");
   constexpr bool kRegs = SZV == kSzInRegs;
-  static_assert(!kRegs || (BITS == 4 && !G64 && (D == 4 || D == 8)), "in-register (s, z): 4-bit, 4 or 8 groups");
+  static_assert(!kRegs || (!G64 && (D == 4 || D == 8)), "in-register (s, z): 128-channel groups, 4 or 8 groups");
   constexpr int R = 4 * XL;          // rows staged per group
   constexpr int kRowHalves = 136;    // 128 + 8
   extern __shared__ __align__(16) char smem[];
